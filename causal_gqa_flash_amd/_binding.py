@@ -1,0 +1,164 @@
+"""ctypes binding of libcgqa.so: argument marshalling only (see include/cgqa.h)."""
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libcgqa.so"
+
+CGQA_OK = 0
+CGQA_EINVAL = 1
+CGQA_EUNSUPPORTED = 2
+CGQA_EHIP = 3
+
+_lib = None
+
+
+class CgqaError(RuntimeError):
+    def __init__(self, call, status, detail=""):
+        self.status = status
+        msg = f"{call} failed with status {status}: {attn_status_string(status)}"
+        super().__init__(msg + (f" ({detail})" if detail else ""))
+
+
+def library_path() -> str:
+    return os.path.join(HERE, _LIB_NAME)
+
+
+def library():
+    """The loaded ctypes library. Raises if it has not been built: no fallback exists."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        i = ctypes.c_int
+        f = ctypes.c_float
+        lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.attn_fwd.restype = i
+        lib.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.attn_bwd_dq.restype = i
+        lib.attn_bwd_dkv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.attn_bwd_dkv.restype = i
+        lib.attn_status_string.argtypes = [i]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.cgqa_last_hip_error.argtypes = []
+        lib.cgqa_last_hip_error.restype = i
+        _lib = lib
+    return _lib
+
+
+def attn_status_string(status: int) -> str:
+    return library().attn_status_string(int(status)).decode()
+
+
+def _check(call, status):
+    if status != CGQA_OK:
+        detail = ""
+        if status == CGQA_EHIP:
+            detail = f"hipError {library().cgqa_last_hip_error()}"
+        raise CgqaError(call, status, detail)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, shape):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dims(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, T, H, d]")
+    B, T, Hq, d = q.shape
+    return B, T, Hq, k.shape[2], d
+
+
+def _scale(scale, d):
+    return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def attn_fwd(q, k, v, scale=None, o=None, lse=None, stream=None):
+    """o [B,T,Hq,d] bf16 and lse [B,Hq,T] fp32 for bf16 q [B,T,Hq,d], k, v [B,T,Hkv,d]."""
+    torch = _torch()
+    B, T, Hq, Hkv, d = _dims(q, k)
+    _need(q, "q", torch.bfloat16, (B, T, Hq, d))
+    _need(k, "k", torch.bfloat16, (B, T, Hkv, d))
+    _need(v, "v", torch.bfloat16, (B, T, Hkv, d))
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.bfloat16, (B, T, Hq, d))
+    _need(lse, "lse", torch.float32, (B, Hq, T))
+    _check("attn_fwd", library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                          B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
+    return o, lse
+
+
+def attn_bwd_dq(q, k, v, o, do, lse, scale=None, delta=None, dq=None, stream=None):
+    """delta [B,Hq,T] fp32 and dq [B,T,Hq,d] fp32."""
+    torch = _torch()
+    B, T, Hq, Hkv, d = _dims(q, k)
+    for t, name in ((q, "q"), (o, "o"), (do, "do")):
+        _need(t, name, torch.bfloat16, (B, T, Hq, d))
+    _need(k, "k", torch.bfloat16, (B, T, Hkv, d))
+    _need(v, "v", torch.bfloat16, (B, T, Hkv, d))
+    _need(lse, "lse", torch.float32, (B, Hq, T))
+    if delta is None:
+        delta = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if dq is None:
+        dq = torch.empty((B, T, Hq, d), dtype=torch.float32, device=q.device)
+    _need(delta, "delta", torch.float32, (B, Hq, T))
+    _need(dq, "dq", torch.float32, (B, T, Hq, d))
+    _check("attn_bwd_dq", library().attn_bwd_dq(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq),
+        B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
+    return delta, dq
+
+
+def attn_bwd_dkv(q, k, v, do, lse, delta, scale=None, dk=None, dv=None, stream=None):
+    """dk, dv [B,T,Hkv,d] fp32. Enqueue after attn_bwd_dq on the same stream."""
+    torch = _torch()
+    B, T, Hq, Hkv, d = _dims(q, k)
+    for t, name in ((q, "q"), (do, "do")):
+        _need(t, name, torch.bfloat16, (B, T, Hq, d))
+    _need(k, "k", torch.bfloat16, (B, T, Hkv, d))
+    _need(v, "v", torch.bfloat16, (B, T, Hkv, d))
+    _need(lse, "lse", torch.float32, (B, Hq, T))
+    _need(delta, "delta", torch.float32, (B, Hq, T))
+    if dk is None:
+        dk = torch.empty((B, T, Hkv, d), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, T, Hkv, d), dtype=torch.float32, device=q.device)
+    _need(dk, "dk", torch.float32, (B, T, Hkv, d))
+    _need(dv, "dv", torch.float32, (B, T, Hkv, d))
+    _check("attn_bwd_dkv", library().attn_bwd_dkv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
+        B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
+    return dk, dv

@@ -1,0 +1,478 @@
+// Backward kernels of causal grouped-query flash attention for gfx950.
+//
+// Method (page "A transformer in PTX", sections "Flash attention" and "The same bits
+// every time"): the backward is two kernels. Both recompute the probabilities from the
+// scores and the saved log-sum-exp instead of storing them. The dQ kernel owns a block
+// of queries; the dK/dV kernel owns a block of keys and loops over all query heads
+// that share its key/value head. No float atomics: every output element has one
+// writer that adds its terms in a fixed order, so two runs give the same bits.
+//
+// For the loss L = sum(O * dO):
+//   P = exp(S - LSE), dP = dO V^T, D_i = sum_j P_ij dP_ij (= dO_i . O_i),
+//   dS = P * (dP - D), dQ = scale * dS K, dK = scale * dS^T Q, dV = P^T dO.
+// In log2 units P = 2^(S * scale * log2(e) - LSE * log2(e)).
+//
+// Precision. All products run on the fp16 matrix core with fp32 accumulation: Q, K,
+// V and dO are converted from bf16 to fp16 (exact for magnitudes in [2^-14, 65504];
+// smaller ones round to fp16 subnormals), and P and dS are rounded to fp16, which
+// carries three more bits than bf16. D has to be accurate to the fp32 level: the one
+// the bf16 output O gives (D~ = dO . O_bf16) is off by the rounding of O, and that error
+// is multiplied by K in dQ and by Q in dK. The dQ kernel therefore forms dS~ with D~
+// (known before its loop), accumulates the exact D = sum_j P_ij dP_ij on the side and
+// K_bar = sum_j P_ij K_j with one more product, and finishes with
+//   dQ = scale * (dS~ K - (D - D~) K_bar),
+// which is the same sum. It writes that exact D to `delta` for the dK/dV kernel.
+//
+// gfx950 layout choices:
+//  * dQ kernel: like the forward, scores are computed transposed (S^T = K Q^T, dP^T =
+//    V dO^T) so each lane owns one query; dS^T and P^T then feed dQ^T += K^T dS^T and
+//    K_bar^T += K^T P^T straight from the accumulator registers, with K^T read from
+//    the row-major K tile by the transposing LDS read.
+//  * dK/dV kernel: scores are computed untransposed (S = Q K^T, dP = dO V^T) so each
+//    lane owns one key; P and dS feed dV^T += dO^T P and dK^T += Q^T dS from the
+//    accumulator registers, with dO^T and Q^T read transposed from the staged tiles.
+//    K and V of the lane's key stay in registers for the whole loop.
+#include "cgqa_device.hpp"
+#include "cgqa_launch.hpp"
+
+namespace cgqa {
+
+// ------------------------------------------------------------------------ dQ kernel
+template <int D, int NQB, int BN, int NW>
+struct DqCfg {
+    static constexpr int kThreads = NW * 64;
+    static constexpr int kBM = NW * 32 * NQB;
+    static constexpr int kKD = D / 16;
+    static constexpr int kNKB = BN / 32;
+    static constexpr int kMB = D / 32;
+    static constexpr int kPitch = D * 2 + 16;     // K and V rows in LDS (fp16)
+    static constexpr int kTile = BN * kPitch;
+    static constexpr int kStage = 2 * kTile;
+    static constexpr int kLds = 2 * kStage;
+    static constexpr int kChunks = BN * D / 8;
+    static constexpr int kPerThread = kChunks / kThreads;
+    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(kChunks % kThreads == 0, "tile load must split evenly over the threads");
+    static_assert(kLds <= 160 * 1024, "LDS budget");
+};
+
+template <int D, int NQB, int BN, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
+    using C = DqCfg<D, NQB, BN, NW>;
+    __shared__ __attribute__((aligned(16))) char smem[C::kLds];
+
+    const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
+    const int bh_count = a.B * Hq;
+    const int bid = blockIdx.x;
+    const int qt = a.n_tiles - 1 - bid / bh_count;
+    const int bh = bid % bh_count;
+    const int b = bh / Hq, h = bh % Hq;
+    const int g = h / (Hq / Hkv);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, hl = lane >> 5;
+    const int q0 = qt * C::kBM;
+    const int qw = q0 + wave * 32 * NQB;
+
+    const size_t q_stride = (size_t)Hq * D;
+    const size_t kv_stride = (size_t)Hkv * D;
+    const size_t qoff = ((size_t)b * T * Hq + h) * D;
+    const uint16_t* kbase = a.k + ((size_t)b * T * Hkv + g) * D;
+    const uint16_t* vbase = a.v + ((size_t)b * T * Hkv + g) * D;
+
+    // Q and dO as B operands (lane: query n, dims 16*kd + 8*hl .. +7), D~ and LSE.
+    f16x8 qreg[NQB][C::kKD], doreg[NQB][C::kKD];
+    float dtilde[NQB], lse2[NQB], dexact[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int row = qw + 32 * qb + n;
+        float part = 0.0f;
+#pragma unroll
+        for (int kd = 0; kd < C::kKD; ++kd) {
+            u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u}, xo = {0u, 0u, 0u, 0u};
+            if (row < T) {
+                const size_t off = qoff + (size_t)row * q_stride + 16 * kd + 8 * hl;
+                xq = load16(a.q + off);
+                xd = load16(a.dO + off);
+                xo = load16(a.o + off);
+            }
+            qreg[qb][kd] = bf16x8_to_f16(xq);
+            doreg[qb][kd] = bf16x8_to_f16(xd);
+            const bf16x8 dv8 = __builtin_bit_cast(bf16x8, xd);
+            const bf16x8 ov8 = __builtin_bit_cast(bf16x8, xo);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) part += (float)dv8[s] * (float)ov8[s];
+        }
+        part += swap_halves(part);
+        dtilde[qb] = part;
+        dexact[qb] = 0.0f;
+        lse2[qb] = row < T ? a.lse[((size_t)b * Hq + h) * T + row] * kLog2e : 0.0f;
+    }
+
+    f32x16 dqacc[NQB][C::kMB], kbar[NQB][C::kMB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int mb = 0; mb < C::kMB; ++mb) { dqacc[qb][mb] = zero16(); kbar[qb][mb] = zero16(); }
+
+    const int kv_end = min(T, q0 + C::kBM);
+    const int ntiles = (kv_end + BN - 1) / BN;
+
+    u32x4 kst[C::kPerThread], vst[C::kPerThread];
+    auto load_tile = [&](int j0) {
+#pragma unroll
+        for (int i = 0; i < C::kPerThread; ++i) {
+            const int c = tid + i * C::kThreads;
+            const int row = c / (D / 8), col = c % (D / 8);
+            const int key = j0 + row;
+            u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+            if (key < T) {
+                xk = load16(kbase + (size_t)key * kv_stride + col * 8);
+                xv = load16(vbase + (size_t)key * kv_stride + col * 8);
+            }
+            kst[i] = xk;
+            vst[i] = xv;
+        }
+    };
+    auto store_tile = [&](int buf) {
+        char* ks = smem + buf * C::kStage;
+        char* vs = ks + C::kTile;
+#pragma unroll
+        for (int i = 0; i < C::kPerThread; ++i) {
+            const int c = tid + i * C::kThreads;
+            const int row = c / (D / 8), col = c % (D / 8);
+            store16(ks + row * C::kPitch + col * 16, bf16x8_to_f16_bits(kst[i]));
+            store16(vs + row * C::kPitch + col * 16, bf16x8_to_f16_bits(vst[i]));
+        }
+    };
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    const int tr_row = (lane & 15) >> 2;
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    for (int jt = 0; jt < ntiles; ++jt) {
+        const int j0 = jt * BN;
+        if (jt + 1 < ntiles) load_tile(j0 + BN);
+        const char* ks = smem + (jt & 1) * C::kStage;
+        const char* vs = ks + C::kTile;
+
+        if (qw + 32 * NQB - 1 >= j0) {
+            f32x16 s[C::kNKB][NQB], dp[C::kNKB][NQB];
+#pragma unroll
+            for (int kb = 0; kb < C::kNKB; ++kb) {
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) { s[kb][qb] = zero16(); dp[kb][qb] = zero16(); }
+#pragma unroll
+                for (int kd = 0; kd < C::kKD; ++kd) {
+                    const int off = (32 * kb + n) * C::kPitch + (16 * kd + 8 * hl) * 2;
+                    const f16x8 ka = lds_read8_f16(ks + off);
+                    const f16x8 va = lds_read8_f16(vs + off);
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb) {
+                        s[kb][qb] = mfma32x32x16(ka, qreg[qb][kd], s[kb][qb]);
+                        dp[kb][qb] = mfma32x32x16(va, doreg[qb][kd], dp[kb][qb]);
+                    }
+                }
+            }
+            // P^T into s, dS~^T into dp; the exact D on the side.
+            const bool need_mask = (j0 + BN - 1 > qw);
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                const int query = qw + 32 * qb + n;
+#pragma unroll
+                for (int kb = 0; kb < C::kNKB; ++kb) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        float p = exp2_fast(fmaf(s[kb][qb][i], a.scale_log2, -lse2[qb]));
+                        if (need_mask) {
+                            const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * hl + (i & 3);
+                            if (key > query) p = 0.0f;
+                        }
+                        dexact[qb] = fmaf(p, dp[kb][qb][i], dexact[qb]);
+                        dp[kb][qb][i] = p * (dp[kb][qb][i] - dtilde[qb]);
+                        s[kb][qb][i] = p;
+                    }
+                }
+            }
+            // dQ~^T += K^T dS~^T and K_bar^T += K^T P^T (B from registers, A = K^T read
+            // transposed from the K tile).
+#pragma unroll
+            for (int kb = 0; kb < C::kNKB; ++kb) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    f16x8 db[NQB], pb[NQB];
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb) {
+                        db[qb] = t == 0 ? pack_lo_f16(dp[kb][qb]) : pack_hi_f16(dp[kb][qb]);
+                        pb[qb] = t == 0 ? pack_lo_f16(s[kb][qb]) : pack_hi_f16(s[kb][qb]);
+                    }
+                    const int r0 = 32 * kb + 16 * t + 4 * hl + tr_row;
+#pragma unroll
+                    for (int mb = 0; mb < C::kMB; ++mb) {
+                        const char* p0 = ks + r0 * C::kPitch + (32 * mb + tr_col) * 2;
+                        const f16x8 kt = concat(lds_read_tr4_f16(p0), lds_read_tr4_f16(p0 + 8 * C::kPitch));
+#pragma unroll
+                        for (int qb = 0; qb < NQB; ++qb) {
+                            dqacc[qb][mb] = mfma32x32x16(kt, db[qb], dqacc[qb][mb]);
+                            kbar[qb][mb] = mfma32x32x16(kt, pb[qb], kbar[qb][mb]);
+                        }
+                    }
+                }
+            }
+        }
+        if (jt + 1 < ntiles) store_tile((jt + 1) & 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int query = qw + 32 * qb + n;
+        const float dfull = dexact[qb] + swap_halves(dexact[qb]);
+        if (query >= T) continue;
+        if (hl == 0) a.delta[((size_t)b * Hq + h) * T + query] = dfull;
+        const float corr = dfull - dtilde[qb];
+        float* drow = a.dq + qoff + (size_t)query * q_stride;
+#pragma unroll
+        for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                f32x4 x;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    x[r] = a.scale * fmaf(-corr, kbar[qb][mb][4 * u + r], dqacc[qb][mb][4 * u + r]);
+                *reinterpret_cast<f32x4*>(drow + 32 * mb + 8 * u + 4 * hl) = x;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------- dK/dV kernel
+template <int D, int BQ, int NW>
+struct DkvCfg {
+    static constexpr int kThreads = NW * 64;
+    static constexpr int kBN = NW * 32;            // keys per workgroup (32 per wave)
+    static constexpr int kKD = D / 16;
+    static constexpr int kMB = D / 32;
+    static constexpr int kQSB = BQ / 32;           // 32-query blocks per staged tile
+    static constexpr int kPitch = D * 2 + 16;      // Q and dO rows in LDS (fp16)
+    static constexpr int kTile = BQ * kPitch;
+    static constexpr int kStage = 2 * kTile + 2 * BQ * 4;   // Q, dO, lse2, delta
+    static constexpr int kLds = 2 * kStage;
+    static constexpr int kChunks = BQ * D / 8;
+    static constexpr int kPerThread = kChunks / kThreads;
+    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(BQ % 32 == 0, "query tile");
+    static_assert(kChunks % kThreads == 0, "tile load must split evenly over the threads");
+    static_assert(2 * BQ <= kThreads, "one thread per staged lse / delta value");
+    static_assert(kLds <= 160 * 1024, "LDS budget");
+};
+
+template <int D, int BQ, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a) {
+    using C = DkvCfg<D, BQ, NW>;
+    __shared__ __attribute__((aligned(16))) char smem[C::kLds];
+
+    const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
+    const int G = Hq / Hkv;
+    const int bg_count = a.B * Hkv;
+    const int bid = blockIdx.x;
+    const int kt = bid / bg_count;                 // key block 0 (the most queries) first
+    const int bg = bid % bg_count;
+    const int b = bg / Hkv, g = bg % Hkv;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, hl = lane >> 5;
+    const int k0 = kt * C::kBN;
+    const int kw = k0 + wave * 32;                 // first key of this wave
+    const int key = kw + n;                        // this lane's key (column)
+
+    const size_t q_stride = (size_t)Hq * D;
+    const size_t kv_stride = (size_t)Hkv * D;
+    const size_t kvoff = ((size_t)b * T * Hkv + g) * D;
+
+    // K and V of the lane's key as B operands (dims 16*kd + 8*hl .. +7).
+    f16x8 kreg[C::kKD], vreg[C::kKD];
+#pragma unroll
+    for (int kd = 0; kd < C::kKD; ++kd) {
+        u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+        if (key < T) {
+            const size_t off = kvoff + (size_t)key * kv_stride + 16 * kd + 8 * hl;
+            xk = load16(a.k + off);
+            xv = load16(a.v + off);
+        }
+        kreg[kd] = bf16x8_to_f16(xk);
+        vreg[kd] = bf16x8_to_f16(xv);
+    }
+
+    f32x16 dkacc[C::kMB], dvacc[C::kMB];
+#pragma unroll
+    for (int mb = 0; mb < C::kMB; ++mb) { dkacc[mb] = zero16(); dvacc[mb] = zero16(); }
+
+    // Steps: heads of the group ascending, then query tiles ascending from the one
+    // holding the first key of this workgroup.
+    const int nqt = (T + BQ - 1) / BQ;
+    const int qt_begin = k0 / BQ;
+    const int per_head = nqt - qt_begin;
+    const int nsteps = k0 < T ? G * per_head : 0;
+
+    u32x4 qst[C::kPerThread], dst[C::kPerThread];
+    float lst = 0.0f;
+    auto load_step = [&](int step) {
+        const int h = g * G + step / per_head;
+        const int qs0 = (qt_begin + step % per_head) * BQ;
+        const size_t hoff = ((size_t)b * T * Hq + h) * D;
+#pragma unroll
+        for (int i = 0; i < C::kPerThread; ++i) {
+            const int c = tid + i * C::kThreads;
+            const int row = c / (D / 8), col = c % (D / 8);
+            const int query = qs0 + row;
+            u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u};
+            if (query < T) {
+                const size_t off = hoff + (size_t)query * q_stride + col * 8;
+                xq = load16(a.q + off);
+                xd = load16(a.dO + off);
+            }
+            qst[i] = xq;
+            dst[i] = xd;
+        }
+        if (tid < 2 * BQ) {
+            const int query = qs0 + (tid % BQ);
+            const size_t off = ((size_t)b * Hq + h) * T + query;
+            if (tid < BQ) lst = query < T ? a.lse[off] * kLog2e : INFINITY;   // P = 0 past T
+            else lst = query < T ? a.delta[off] : 0.0f;
+        }
+    };
+    auto store_step = [&](int buf) {
+        char* qs = smem + buf * C::kStage;
+        char* ds = qs + C::kTile;
+        float* ls = reinterpret_cast<float*>(ds + C::kTile);
+#pragma unroll
+        for (int i = 0; i < C::kPerThread; ++i) {
+            const int c = tid + i * C::kThreads;
+            const int row = c / (D / 8), col = c % (D / 8);
+            store16(qs + row * C::kPitch + col * 16, bf16x8_to_f16_bits(qst[i]));
+            store16(ds + row * C::kPitch + col * 16, bf16x8_to_f16_bits(dst[i]));
+        }
+        if (tid < 2 * BQ) ls[tid] = lst;
+    };
+
+    if (nsteps > 0) {
+        load_step(0);
+        store_step(0);
+    }
+    __syncthreads();
+
+    const int tr_row = (lane & 15) >> 2;
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    for (int step = 0; step < nsteps; ++step) {
+        if (step + 1 < nsteps) load_step(step + 1);
+        const char* qs = smem + (step & 1) * C::kStage;
+        const char* ds = qs + C::kTile;
+        const float* lse2s = reinterpret_cast<const float*>(ds + C::kTile);
+        const float* dels = lse2s + BQ;
+        const int qs0 = (qt_begin + step % per_head) * BQ;
+
+#pragma unroll
+        for (int sb = 0; sb < C::kQSB; ++sb) {
+            const int qb0 = qs0 + 32 * sb;             // first query of this block
+            if (qb0 + 31 < kw) continue;               // every query precedes every key
+            f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int kd = 0; kd < C::kKD; ++kd) {
+                const int off = (32 * sb + n) * C::kPitch + (16 * kd + 8 * hl) * 2;
+                s = mfma32x32x16(lds_read8_f16(qs + off), kreg[kd], s);
+                dp = mfma32x32x16(lds_read8_f16(ds + off), vreg[kd], dp);
+            }
+            // Register i holds query qb0 + 8*(i/4) + 4*hl + i%4 of the lane's key.
+            const bool need_mask = (qb0 < kw + 31);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = 32 * sb + 8 * u + 4 * hl;
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + r);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dels + r);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * u + e;
+                    float p = exp2_fast(fmaf(s[i], a.scale_log2, -l4[e]));
+                    if (need_mask && key > qb0 + 8 * u + 4 * hl + e) p = 0.0f;
+                    s[i] = p;
+                    dp[i] = p * (dp[i] - d4[e]);           // dS
+                }
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per instruction.
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const f16x8 pb = t == 0 ? pack_lo_f16(s) : pack_hi_f16(s);
+                const f16x8 sb8 = t == 0 ? pack_lo_f16(dp) : pack_hi_f16(dp);
+                const int r0 = 32 * sb + 16 * t + 4 * hl + tr_row;
+#pragma unroll
+                for (int mb = 0; mb < C::kMB; ++mb) {
+                    const int off = r0 * C::kPitch + (32 * mb + tr_col) * 2;
+                    const f16x8 dot = concat(lds_read_tr4_f16(ds + off), lds_read_tr4_f16(ds + off + 8 * C::kPitch));
+                    const f16x8 qt8 = concat(lds_read_tr4_f16(qs + off), lds_read_tr4_f16(qs + off + 8 * C::kPitch));
+                    dvacc[mb] = mfma32x32x16(dot, pb, dvacc[mb]);
+                    dkacc[mb] = mfma32x32x16(qt8, sb8, dkacc[mb]);
+                }
+            }
+        }
+        if (step + 1 < nsteps) store_step((step + 1) & 1);
+        __syncthreads();
+    }
+
+    if (key < T) {
+        float* dkrow = a.dk + kvoff + (size_t)key * kv_stride;
+        float* dvrow = a.dv + kvoff + (size_t)key * kv_stride;
+#pragma unroll
+        for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                f32x4 xk, xv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    xk[r] = dkacc[mb][4 * u + r] * a.scale;
+                    xv[r] = dvacc[mb][4 * u + r];
+                }
+                *reinterpret_cast<f32x4*>(dkrow + 32 * mb + 8 * u + 4 * hl) = xk;
+                *reinterpret_cast<f32x4*>(dvrow + 32 * mb + 8 * u + 4 * hl) = xv;
+            }
+    }
+}
+
+template <int D, int NQB, int BN, int NW>
+static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream) {
+    using C = DqCfg<D, NQB, BN, NW>;
+    BwdArgs x = a;
+    x.n_tiles = (a.T + C::kBM - 1) / C::kBM;
+    const long blocks = (long)x.n_tiles * a.B * a.Hq;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, NQB, BN, NW>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
+                       stream, x);
+    return hipGetLastError();
+}
+
+template <int D, int BQ, int NW>
+static hipError_t launch_dkv_t(const BwdArgs& a, hipStream_t stream) {
+    using C = DkvCfg<D, BQ, NW>;
+    BwdArgs x = a;
+    x.n_tiles = (a.T + C::kBN - 1) / C::kBN;
+    const long blocks = (long)x.n_tiles * a.B * a.Hkv;
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NW>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
+                       stream, x);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
+    if (a.d == 64) return launch_dq_t<64, 1, 64, 4>(a, stream);
+    return launch_dq_t<128, 1, 32, 4>(a, stream);
+}
+
+hipError_t launch_bwd_dkv(const BwdArgs& a, hipStream_t stream) {
+    if (a.d == 64) return launch_dkv_t<64, 64, 4>(a, stream);
+    return launch_dkv_t<128, 64, 4>(a, stream);
+}
+
+}  // namespace cgqa

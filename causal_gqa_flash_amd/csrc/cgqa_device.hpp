@@ -1,0 +1,124 @@
+// Device-side building blocks for the gfx950 attention kernels: vector types, the
+// bf16 matrix-core instruction, the transposing LDS read and small lane helpers.
+//
+// Lane maps of v_mfma_f32_32x32x16_bf16 (wave64), as measured on gfx950:
+//   A (32 x 16): lane l holds row m = l % 32, eight k slots of group h = l / 32.
+//   B (16 x 32): lane l holds column n = l % 32, eight k slots of group h = l / 32.
+//   A slot (h, s) multiplies B slot (h, s): which k a slot stands for is the
+//   caller's choice, as long as A and B agree.
+//   C (32 x 32): lane l register i holds row 8*(i/4) + 4*h + i%4, column n.
+// ds_read_b64_tr_b16 works on groups of 16 lanes: if lane j of a group points at
+// row j/4, columns 4*(j%4)..+3 of a 4 x 16 bf16 block, lane i of the group receives
+// column i, rows 0..3. That is a column read of a row-major tile, which is how a
+// matrix stored [k][n] becomes an MFMA operand whose slots run along k.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cgqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __fp16 fp16x4_raw __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) fp16x4_raw lds_f16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The fp16 variant has the same lane maps.
+__device__ __forceinline__ f32x16 mfma32x32x16(const f16x8& a, const f16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+    return z;
+}
+
+// 16-byte LDS read of eight bf16 (an A or B operand whose slots run along a row).
+__device__ __forceinline__ bf16x8 lds_read8(const char* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// Transposing LDS read: see the lane map above. `p` is this lane's source address.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+__device__ __forceinline__ f16x8 lds_read8_f16(const char* p) {
+    return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ f16x4 lds_read_tr4_f16(const char* p) {
+    return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4*)(p)));
+}
+
+__device__ __forceinline__ bf16x8 concat(const bf16x4& lo, const bf16x4& hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f16x8 concat(const f16x4& lo, const f16x4& hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Eight bf16 values (as loaded, two per 32-bit word, the first in the low half) to
+// fp16. bf16 -> fp32 is exact (the bf16 pattern is the upper half of the fp32 one);
+// fp32 -> fp16 (v_cvt_pk_f16_f32, round to nearest even) is exact for magnitudes in
+// [2^-14, 65504], since a bf16 value has only 8 significant bits.
+__device__ __forceinline__ f16x8 bf16x8_to_f16(const u32x4& w) {
+    f32x8 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+        f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+    }
+    return __builtin_convertvector(f, f16x8);
+}
+__device__ __forceinline__ u32x4 bf16x8_to_f16_bits(const u32x4& w) {
+    return __builtin_bit_cast(u32x4, bf16x8_to_f16(w));
+}
+
+// Eight accumulator registers (base .. base+7) rounded to bf16 (round to nearest
+// even, v_cvt_pk_bf16_f32), in register order.
+__device__ __forceinline__ bf16x8 pack_lo(const f32x16& c) {
+    return __builtin_convertvector(c.lo, bf16x8);
+}
+__device__ __forceinline__ bf16x8 pack_hi(const f32x16& c) {
+    return __builtin_convertvector(c.hi, bf16x8);
+}
+// The same, rounded to fp16 (round to nearest even).
+__device__ __forceinline__ f16x8 pack_lo_f16(const f32x16& c) {
+    return __builtin_convertvector(c.lo, f16x8);
+}
+__device__ __forceinline__ f16x8 pack_hi_f16(const f32x16& c) {
+    return __builtin_convertvector(c.hi, f16x8);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by the lane 32 positions away (the other k-group of the same column).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store16(char* p, const u32x4& v) {
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+
+}  // namespace cgqa

@@ -1,0 +1,95 @@
+/*
+ * cgqa: causal grouped-query flash attention for AMD MI355X (gfx950).
+ *
+ * The operation is the causal softmax attention of a Llama-style decoder with
+ * grouped-query heads (page "A transformer in PTX", section "The model": several query
+ * heads share one key/value head), computed as flash attention (section "Flash
+ * attention": the T x T score matrix is never written out; each row keeps a running
+ * max and sum in log2 units; the forward saves each row's log-sum-exp so the backward
+ * can recompute the probabilities), with a two-kernel deterministic backward (section
+ * "The same bits every time": dQ per block of queries; dK/dV per block of keys looping
+ * over the query heads that share the key/value head; no float atomics, so two runs
+ * give identical bits).
+ *
+ * Shapes and layout (all tensors contiguous, row-major, owned by the caller):
+ *   q, o, dO : [B][T][Hq][d]   bfloat16 (passed as uint16_t bit patterns)
+ *   k, v     : [B][T][Hkv][d]  bfloat16
+ *   lse      : [B][Hq][T]      float32, natural-log log-sum-exp of each row of
+ *                              scale * q.k over keys 0..i (causal, inclusive)
+ *   delta    : [B][Hq][T]      float32, D_i = sum_c dO[i,c] * O[i,c]
+ *   dq       : [B][T][Hq][d]   float32
+ *   dk, dv   : [B][T][Hkv][d]  float32
+ * Query head h uses key/value head h / (Hq / Hkv). Query i sees keys 0..i.
+ * d must be 64 or 128. Every pointer must be 16-byte aligned device memory.
+ *
+ * Every call only enqueues work on `stream` (a hipStream_t; NULL = the default
+ * stream) and returns; outputs are valid once the caller synchronises with the stream.
+ * A fault while the kernels run surfaces at that synchronisation, not in the return
+ * value. Calls allocate nothing, keep no state between calls and may be made from
+ * several host threads at once. Outputs must not overlap inputs or each other.
+ * B == 0 or T == 0 is an empty problem: the call succeeds and touches nothing.
+ *
+ * Return value: CGQA_OK (0) or one of the codes below. All argument checks happen
+ * before any HIP call, so a rejected call has touched neither the device nor the
+ * stream.
+ */
+#ifndef CGQA_H
+#define CGQA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    CGQA_OK = 0,
+    /* null pointer with non-empty sizes, negative size, Hq or Hkv < 1, Hq % Hkv != 0,
+       scale not finite or not positive, an element count of 2^31 or more,
+       or an output that overlaps another buffer */
+    CGQA_EINVAL = 1,
+    /* head dimension other than 64 or 128, or a pointer not 16-byte aligned */
+    CGQA_EUNSUPPORTED = 2,
+    /* the kernel launch was refused by the HIP runtime (cgqa_last_hip_error() tells
+       which HIP error, for the calling thread) */
+    CGQA_EHIP = 3
+};
+
+/* Forward (section "Flash attention"): o = softmax(scale * q k^T, causal) v per query
+ * head, and lse = the natural-log log-sum-exp of each row of scaled scores.
+ * Reads q, k, v; overwrites o and lse. */
+int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+             uint16_t* o, float* lse,
+             int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
+
+/* Backward, query side (section "The same bits every time": one owner per block of
+ * queries). For the loss L = sum(O * dO): recomputes P from q, k and lse, writes
+ * delta = rowsum(dO * o) (from the bf16 o given) and dq = dL/dq.
+ * Reads q, k, v, o, dO, lse; overwrites delta and dq. */
+int attn_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                const uint16_t* o, const uint16_t* dO, const float* lse,
+                float* delta, float* dq,
+                int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
+
+/* Backward, key side (same section: one owner per block of keys, looping over the
+ * query heads that share its key/value head in ascending order, then over query
+ * blocks in ascending order). Writes dk = dL/dk and dv = dL/dv, summed over the
+ * group. Reads the delta written by attn_bwd_dq, so it must be enqueued after that
+ * call on the same stream (or after an event recorded behind it).
+ * Reads q, k, v, dO, lse, delta; overwrites dk and dv. */
+int attn_bwd_dkv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                 const uint16_t* dO, const float* lse, const float* delta,
+                 float* dk, float* dv,
+                 int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
+
+/* Static description of a return code (never NULL). */
+const char* attn_status_string(int status);
+
+/* The HIP error code behind the calling thread's last CGQA_EHIP (0 if none). */
+int cgqa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CGQA_H */

@@ -1,0 +1,175 @@
+"""Parity of the HIP path (through the C-ABI) with the fp64 CPU oracle, element by
+element, on seeded bf16 inputs: small shapes that span several tiles and ragged tails,
+every workload at full size (oracle on sampled (batch, kv head) slices, which are
+independent), special inputs with closed forms, and determinism."""
+import numpy as np
+import pytest
+
+import synthetic_inputs as si
+from parity_util import (LSE_ABS, check_all, compare, gpu_run, oracle_run, slice_outputs,
+                         to_device, workload_scale)
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+SMALL = [
+    # (B, T, Hq, Hkv, d, seed, qk_mult)
+    (1, 64, 6, 2, 64, 1, 1.0),
+    (1, 1, 6, 2, 64, 2, 1.0),
+    (2, 2, 4, 1, 64, 3, 1.0),
+    (1, 31, 3, 3, 64, 4, 1.0),
+    (2, 33, 6, 2, 64, 5, 1.0),
+    (1, 65, 4, 2, 128, 6, 1.0),
+    (3, 100, 8, 2, 64, 7, 2.0),
+    (1, 127, 2, 1, 128, 8, 1.0),
+    (2, 129, 6, 2, 64, 9, 1.0),
+    (1, 200, 8, 8, 128, 10, 2.0),
+    (1, 257, 12, 4, 64, 11, 1.0),
+    (2, 300, 4, 1, 128, 12, 1.0),
+    (1, 1000, 6, 2, 64, 13, 1.0),
+]
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,d,seed,mult", SMALL)
+def test_parity_small(B, T, Hq, Hkv, d, seed, mult):
+    _log(f"parity small B={B} T={T} Hq={Hq} Hkv={Hkv} d={d} seed={seed}")
+    x = si.make_inputs(B, T, Hq, Hkv, d, seed, mult)
+    scale = workload_scale(d)
+    got = gpu_run(x, scale)
+    want = oracle_run(x, scale)
+    ok, msg = check_all(got, want, keys=("o", "lse", "delta", "dq", "dk", "dv"), inputs=x)
+    assert ok, msg
+
+
+@pytest.mark.parametrize("w", si.WORKLOADS, ids=[w.name for w in si.WORKLOADS])
+def test_parity_full_workload(w):
+    """Full-size launch; the oracle checks the first and the last (batch, kv head) slice
+    (and the whole problem for the two smallest workloads)."""
+    _log(f"parity full {w.name}")
+    x = si.make_workload_inputs(w, seed=si.WORKLOADS.index(w) + 1)
+    got = gpu_run(x, w.scale)
+    if w.B * w.T <= 8 * 512:
+        want = oracle_run(x, w.scale)
+        ok, msg = check_all(got, want)
+        assert ok, msg
+        return
+    for b, g in ((0, 0), (w.B - 1, w.Hkv - 1)):
+        xs = si.slice_group(x, w.Hq, w.Hkv, b, g)
+        want = oracle_run(xs, w.scale)
+        ok, msg = check_all(slice_outputs(got, w.Hq, w.Hkv, b, g), want)
+        assert ok, f"slice b={b} g={g}: {msg}"
+
+
+@pytest.mark.parametrize("w", si.WORKLOADS[:4], ids=[w.name for w in si.WORKLOADS[:4]])
+def test_zero_queries_closed_form(w):
+    """Q = 0: every causal row is uniform, so O_i is the prefix mean of V (bf16 rounded)
+    and LSE_i = ln(i + 1); checked on every element at full size."""
+    _log(f"zero queries {w.name}")
+    x = si.make_workload_inputs(w, seed=21, with_do=False)
+    x["q"][:] = 0
+    got = gpu_run(x, w.scale, backward=False)
+    v = si.bf16_bits_to_f32(x["v"]).astype(np.float64)
+    cnt = np.arange(1, w.T + 1, dtype=np.float64)
+    prefix = np.cumsum(v, axis=1) / cnt[None, :, None, None]          # [B,T,Hkv,d]
+    want_o = np.repeat(prefix, w.G, axis=2)
+    ok, msg = compare("o", got["o"], want_o)
+    assert ok, msg
+    ok, msg = compare("lse", got["lse"], np.broadcast_to(np.log(cnt), got["lse"].shape),
+                      rel_l2=None, max_abs=LSE_ABS)
+    assert ok, msg
+
+
+def test_constant_values_give_constant_output():
+    """Rows of P sum to one: V equal to a bf16-exact constant per channel gives O equal
+    to it (up to the rounding of the sum), at every position."""
+    B, T, Hq, Hkv, d = 2, 700, 6, 2, 64
+    x = si.make_inputs(B, T, Hq, Hkv, d, seed=30, qk_mult=2.0, with_do=False)
+    c = si.f32_to_bf16_bits(np.linspace(-3, 3, d).astype(np.float32))
+    x["v"][:] = c
+    got = gpu_run(x, workload_scale(d), backward=False)
+    want = np.broadcast_to(si.bf16_bits_to_f32(c).astype(np.float64), got["o"].shape)
+    ok, msg = compare("o", got["o"], want, rel_l2=1e-3, max_abs=2e-2)
+    assert ok, msg
+
+
+def test_row_zero_closed_form():
+    B, T, Hq, Hkv, d = 3, 130, 8, 2, 128
+    x = si.make_inputs(B, T, Hq, Hkv, d, seed=31, with_do=False)
+    scale = workload_scale(d)
+    got = gpu_run(x, scale, backward=False)
+    q = si.bf16_bits_to_f32(x["q"]).astype(np.float64)
+    k = si.bf16_bits_to_f32(x["k"]).astype(np.float64)
+    v = si.bf16_bits_to_f32(x["v"]).astype(np.float64)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        np.testing.assert_array_equal(got["o"][:, 0, h], v[:, 0, g])     # bf16 exact
+        want = scale * np.sum(q[:, 0, h] * k[:, 0, g], axis=-1)
+        assert np.max(np.abs(got["lse"][:, h, 0] - want)) <= LSE_ABS
+
+
+def _bits(t):
+    import torch
+    return t.contiguous().view(torch.uint8).cpu().numpy().copy()
+
+
+def test_bitwise_repeatable():
+    """Two runs of the three calls, with unrelated device work in between, give
+    identical bits for every output."""
+    import torch
+    import causal_gqa_flash_amd as cg
+    w = si.WORKLOADS[2]
+    _log(f"determinism {w.name}")
+    x = to_device(si.make_workload_inputs(w, seed=3))
+    runs = []
+    for rep in range(2):
+        o, lse = cg.attn_fwd(x["q"], x["k"], x["v"], scale=w.scale)
+        delta, dq = cg.attn_bwd_dq(x["q"], x["k"], x["v"], o, x["do"], lse, scale=w.scale)
+        dk, dv = cg.attn_bwd_dkv(x["q"], x["k"], x["v"], x["do"], lse, delta, scale=w.scale)
+        torch.cuda.synchronize()
+        runs.append([_bits(t) for t in (o, lse, delta, dq, dk, dv)])
+        junk = torch.randn(4096, 4096, device="cuda")
+        (junk @ junk).sum().item()
+    for a, b in zip(*runs):
+        assert np.array_equal(a, b)
+
+
+def test_batch_permutation_is_exact():
+    """Batches are independent: permuting them permutes the outputs bit for bit."""
+    B, T, Hq, Hkv, d = 4, 300, 6, 2, 64
+    x = si.make_inputs(B, T, Hq, Hkv, d, seed=32)
+    perm = [2, 0, 3, 1]
+    y = {n: np.ascontiguousarray(a[perm]) for n, a in x.items()}
+    gx = gpu_run(x, 0.125)
+    gy = gpu_run(y, 0.125)
+    for n in gx:
+        np.testing.assert_array_equal(gx[n][perm], gy[n])
+
+
+def test_empty_problems():
+    import torch
+    import causal_gqa_flash_amd as cg
+    for B, T in ((0, 16), (2, 0)):
+        q = torch.zeros((B, T, 4, 64), dtype=torch.bfloat16, device="cuda")
+        k = torch.zeros((B, T, 2, 64), dtype=torch.bfloat16, device="cuda")
+        o, lse = cg.attn_fwd(q, k, k)
+        delta, dq = cg.attn_bwd_dq(q, k, k, o, q, lse)
+        dk, dv = cg.attn_bwd_dkv(q, k, k, q, lse, delta)
+        torch.cuda.synchronize()
+        assert dk.shape == (B, T, 2, 64)
+
+
+def test_side_stream():
+    """Work enqueued on a non-default stream gives the same bits as on the default one."""
+    import torch
+    w = si.WORKLOADS[1]
+    x = si.make_workload_inputs(w, seed=40)
+    a = gpu_run(x, w.scale)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = gpu_run(x, w.scale, stream=s)
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n])
