@@ -1,0 +1,201 @@
+"""Throughput of the causal grouped-query flash attention hot path on one MI355X.
+
+A step is one pass of the whole path over one synthetic batch: attn_fwd, then
+attn_bwd_dq, then attn_bwd_dkv, all through the C-ABI, with inputs resident in HBM.
+The workload is B=16, T=1024, Hq=6, Hkv=2, d=64 (bf16 N(0,1) inputs, seeded).
+
+Flop convention (causal pairs only, pairs = B*Hq*T*(T+1)/2; diagonal-tile waste and
+the backward's recomputation are not credited):
+  forward  = 4*d per pair (S = Q K^T and P V),
+  backward = 10*d per pair (five contractions: S, dP, dQ, dK, dV),
+  step     = 14*d per pair.
+Per kernel, for the roofline line: attn_fwd 4*d, attn_bwd_dq 6*d (S, dP, dQ),
+attn_bwd_dkv 8*d (S, dP, dV, dK) per pair.
+
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 dense bf16/fp16 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = "B16_T1024_Hq6_Hkv2_d64"
+KERNEL_SOURCES = ["causal_gqa_flash_amd/csrc/attn_fwd.hip", "causal_gqa_flash_amd/csrc/attn_bwd.hip",
+                  "causal_gqa_flash_amd/csrc/cgqa_device.hpp", "causal_gqa_flash_amd/build.py"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_B16_T1024_Hq6_Hkv2_d64.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the kernels as they are now; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, budget_s):
+    """The fp64 CPU oracle (as it is) on whole (batch, kv head) slices of the workload,
+    forward and backward, until about budget_s seconds have passed."""
+    import numpy as np
+    import oracle
+    import synthetic_inputs as si
+    threads = oracle.default_threads()
+    slices = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    done, t0 = 0, time.perf_counter()
+    for b, g in slices:
+        xs = si.slice_group(x, w.Hq, w.Hkv, b, g)
+        f = {n: oracle.bf16_to_f64(a) for n, a in xs.items()}
+        oracle.attn_bwd(f["q"], f["k"], f["v"], f["do"], w.scale, threads=threads)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    secs = time.perf_counter() - t0
+    pairs = done * w.G * w.T * (w.T + 1) // 2
+    tflops = 14 * w.d * pairs / secs / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(secs, 3),
+            "sample": f"{done} of {len(slices)} (batch, kv head) slices of {w.name}, forward and "
+                      f"backward in fp64, {threads} threads; same 14*d flop/pair convention"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--repeats", type=int, default=5, help="timed repeats; the median is reported")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs on a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import causal_gqa_flash_amd as cg
+    import synthetic_inputs as si
+
+    w = si.WORKLOAD_BY_NAME[WORKLOAD]
+    x = si.make_workload_inputs(w, seed=3)
+    dev = {n: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for n, a in x.items()}
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device="cuda")
+    delta = torch.empty_like(lse)
+    dq = torch.empty((w.B, w.T, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    dk = torch.empty((w.B, w.T, w.Hkv, w.d), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        cg.attn_fwd(q, k, v, scale=w.scale, o=o, lse=lse, stream=stream)
+
+    def bwd_dq():
+        cg.attn_bwd_dq(q, k, v, o, do, lse, scale=w.scale, delta=delta, dq=dq, stream=stream)
+
+    def bwd_dkv():
+        cg.attn_bwd_dkv(q, k, v, do, lse, delta, scale=w.scale, dk=dk, dv=dv, stream=stream)
+
+    def step():
+        fwd()
+        bwd_dq()
+        bwd_dkv()
+
+    def timed(fn, n):
+        """Median over repeats of the mean ms per call of n back-to-back calls, timed
+        with HIP events on the stream the kernels run on."""
+        per = []
+        for _ in range(args.repeats):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / n)
+        return float(np.median(per))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Whole-step timing: exactly `steps` steps between synchronisations.
+    ms_step = timed(step, args.steps)
+    # Per-kernel average launch durations (same stream, back-to-back launches).
+    ms_k = {"attn_fwd": timed(fwd, args.steps), "attn_bwd_dq": timed(bwd_dq, args.steps),
+            "attn_bwd_dkv": timed(bwd_dkv, args.steps)}
+
+    pairs = w.causal_pairs
+    fl = {"attn_fwd": 4 * w.d * pairs, "attn_bwd_dq": 6 * w.d * pairs, "attn_bwd_dkv": 8 * w.d * pairs}
+    step_flops = 14 * w.d * pairs
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    fwd_tflops = fl["attn_fwd"] / (ms_k["attn_fwd"] * 1e-3) / 1e12
+    bwd_ms = ms_k["attn_bwd_dq"] + ms_k["attn_bwd_dkv"]
+    bwd_tflops = 10 * w.d * pairs / (bwd_ms * 1e-3) / 1e12
+    dom = max(ms_k, key=ms_k.get)
+    achieved = fl[dom] / (ms_k[dom] * 1e-3) / 1e12
+    traffic = measured_traffic(dom)
+    kernels = {}
+    for name in ms_k:
+        a = fl[name] / (ms_k[name] * 1e-3) / 1e12
+        kernels[name] = {"ms": round(ms_k[name], 5), "tflops": round(a, 2),
+                         "frac": round(a / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(name)}
+
+    out = {
+        "metric": "causal attention TFLOP/s fwd and fwd+bwd, % of bf16 MFMA peak, 1xMI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
+                   "pass": "fwd+bwd", "inputs": "bf16 N(0,1), seed 3"},
+        "fwd_tflops": round(fwd_tflops, 2),
+        "fwd_pct_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+        "bwd_tflops": round(bwd_tflops, 2),
+        "fwdbwd_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "compute": "fwd bf16 matrix core; bwd fp16 matrix core; fp32 accumulation and softmax",
+        "kernels": kernels,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
