@@ -11,8 +11,12 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for all device code; the host pass
 # reports that it does not know the feature, which is harmless.
+# Matrix-core accumulators are kept in ordinary VGPRs (amdgpu-mfma-vgpr-form): the
+# softmax works on them with the vector ALU, and AGPR<->VGPR copies would cost more
+# vector instructions than the math itself.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function"]
 
 

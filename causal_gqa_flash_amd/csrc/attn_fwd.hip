@@ -2,53 +2,83 @@
 //
 // Method (page "A transformer in PTX", section "Flash attention"): one workgroup owns
 // a block of queries of one head and walks the key blocks up to the diagonal. The
-// score matrix is never written to memory: each query keeps a running max m and sum l
-// (online softmax) in log2 units, the scores being multiplied once by
+// score matrix is never written to memory: each query keeps a running reference max m
+// and sum l (online softmax) in log2 units, the scores being multiplied once by
 // scale * log2(e) and each probability being 2^(s - m). At the end O = acc / l and the
 // row's log-sum-exp, converted to natural log, is saved for the backward.
 //
 // gfx950 design (not the page's sm_120 one):
 //  * The scores are computed transposed, S^T = K Q^T, on the 32x32x16 bf16 matrix
 //    core. Each lane then owns one query (a column) and 16 keys of every 32-key block,
-//    so a row max or sum is an in-lane reduction plus one swap with the lane 32 away.
+//    so a row reduction is an in-lane reduction plus one swap with the lane 32 away.
 //  * The same accumulator registers, rounded to bf16, are the B operand of
 //    O^T += V^T P^T: no trip through LDS for P (the role the pages give to their
 //    C-fragment to A-fragment match). V^T comes from the row-major V tile through the
 //    transposing LDS read.
-//  * Q stays in registers for the whole loop. K and V tiles are staged in LDS, double
-//    buffered, loaded with 16-byte global loads; rows are padded so the 16-byte row
-//    reads (K) and the transposing reads (V) spread over the banks.
+//  * The reference max is not updated tile by tile. Softmax is invariant to the
+//    reference (O = sum p v / sum p and LSE = m + log2 l hold for any m), so m is taken
+//    from the first key block (which holds key 0 for every query) and kept while every
+//    probability stays below 2^40. Only when a block's sum shows a larger value (a
+//    score 40 log2 units above m) does the wave recompute that block's scores, move m
+//    to the new row max and rescale l and the accumulators. This keeps the per-score
+//    max and the per-block rescale off the vector ALU, which limits this kernel at
+//    d = 64: one exp2, one fma, one add and half a convert per score remain.
+//  * K and V tiles go straight from global memory to LDS (global_load_lds_dwordx4, no
+//    staging registers) into a ring of three stages, two tiles ahead of the compute.
+//    A direct load writes 1 KB of consecutive LDS per instruction, so rows cannot be
+//    padded; instead the 16-byte chunks of each row are XOR-swizzled (see
+//    chunk_swizzle) so that both the 16-byte row reads of K and the transposing reads
+//    of V spread over the 64 banks.
 //  * Work order: the heaviest query blocks (the ones with the most keys) start first.
 #include "cgqa_device.hpp"
 #include "cgqa_launch.hpp"
 
 namespace cgqa {
 
+// Physical 16-byte slot of logical chunk c in LDS row r is c ^ chunk_swizzle<D>(r).
+// LDS serves 64 banks x 4 bytes per clock: a D=64 row (128 B) is half a bank window,
+// a D=128 row a whole one. For 16 lanes reading the same chunk of 16 consecutive rows
+// (the K operand) every (row parity, slot) pair, resp. slot, must differ; for a
+// transposing read (4 consecutive rows, an aligned pair of chunks) the slot pairs of
+// rows that share a bank window must differ. Both hold for these maps.
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int r) {
+    if constexpr (D == 64) {
+        const int u = (r >> 1) & 7;
+        return ((u & 1) << 2) | (((u >> 2) & 1) << 1) | ((u >> 1) & 1);
+    } else {
+        return ((r & 7) << 1) | ((r >> 3) & 1);
+    }
+}
+
 template <int D, int NQB, int BN, int NW>
 struct FwdCfg {
     static constexpr int kThreads = NW * 64;
+    static constexpr int kBN = BN;                  // keys per tile
     static constexpr int kBM = NW * 32 * NQB;       // queries per workgroup
     static constexpr int kKD = D / 16;              // k-steps over the head dimension
-    static constexpr int kNKB = BN / 32;            // 32-key blocks per tile
+    static constexpr int kNKB = kBN / 32;           // 32-key blocks per tile
     static constexpr int kMB = D / 32;              // 32-dim blocks of the output
-    static constexpr int kKPitch = D * 2 + 16;      // bytes per K row in LDS
-    static constexpr int kVPitch = D * 2 + 32;      // bytes per V row in LDS
-    static constexpr int kKBytes = BN * kKPitch;
-    static constexpr int kVBytes = BN * kVPitch;
-    static constexpr int kStage = kKBytes + kVBytes;
-    static constexpr int kLds = 2 * kStage;
-    static constexpr int kChunks = BN * D / 8;      // 16-byte chunks per tile and tensor
-    static constexpr int kPerThread = kChunks / kThreads;
+    static constexpr int kRow = D * 2;              // bytes per K or V row in LDS
+    static constexpr int kTile = kBN * kRow;        // bytes per K (or V) tile
+    static constexpr int kStages = 3;
+    static constexpr int kStage = 2 * kTile;        // K then V
+    static constexpr int kLds = kStages * kStage;
+    static constexpr int kLoadsPerTensor = kTile / 1024 / NW;   // 1 KB per wave instruction
+    static constexpr int kLoadsPerTile = 2 * kLoadsPerTensor;    // per wave
+    static constexpr int kRowsPerLoad = 1024 / kRow;
     static_assert(D == 64 || D == 128, "head dim");
-    static_assert(BN % 32 == 0 && BN >= 32, "key tile");
-    static_assert(kChunks % kThreads == 0, "tile load must split evenly over the threads");
+    static_assert(kTile % (1024 * NW) == 0, "tile load must split evenly over the waves");
     static_assert(kLds <= 160 * 1024, "LDS budget");
 };
+
+// Probabilities above this trigger a move of the reference max.
+constexpr float kRescaleLimit = 1099511627776.0f;   // 2^40
 
 template <int D, int NQB, int BN, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     using C = FwdCfg<D, NQB, BN, NW>;
-    __shared__ __attribute__((aligned(16))) char smem[C::kLds];
+    __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
 
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
     const int bh_count = a.B * Hq;
@@ -63,12 +93,43 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     const int n = lane & 31, hl = lane >> 5;
     const int q0 = qt * C::kBM;
     const int qw = q0 + wave * 32 * NQB;   // first query of this wave
+    const float c = a.scale_log2;
 
     const size_t q_stride = (size_t)Hq * D;     // elements between consecutive t
     const size_t kv_stride = (size_t)Hkv * D;
     const uint16_t* qbase = a.q + ((size_t)b * T * Hq + h) * D;
     const uint16_t* kbase = a.k + ((size_t)b * T * Hkv + g) * D;
     const uint16_t* vbase = a.v + ((size_t)b * T * Hkv + g) * D;
+
+    const int kv_end = min(T, q0 + C::kBM);            // keys 0 .. kv_end-1 are needed
+    const int ntiles = (kv_end + C::kBN - 1) / C::kBN;
+
+    // Tile loader: wave instruction i of this wave fills rows
+    // kRowsPerLoad * (wave * kLoadsPerTensor + i) + lane / (kRow/16) of the tile, slot
+    // lane % (kRow/16), with the logical chunk that the swizzle puts there. Rows past
+    // T read row T-1 (finite data; those keys are masked for every real query).
+    const int ld_slot = lane % (C::kRow / 16);
+    int ld_row[C::kLoadsPerTensor], ld_chunk[C::kLoadsPerTensor];
+#pragma unroll
+    for (int i = 0; i < C::kLoadsPerTensor; ++i) {
+        ld_row[i] = C::kRowsPerLoad * (wave * C::kLoadsPerTensor + i) + lane / (C::kRow / 16);
+        ld_chunk[i] = ld_slot ^ chunk_swizzle<D>(ld_row[i]);
+    }
+    auto issue_tile = [&](int jt) {
+        char* ks = smem + (jt % C::kStages) * C::kStage;
+        char* vs = ks + C::kTile;
+#pragma unroll
+        for (int i = 0; i < C::kLoadsPerTensor; ++i) {
+            const int key = min(jt * C::kBN + ld_row[i], T - 1);
+            const size_t off = (size_t)key * kv_stride + ld_chunk[i] * 8;
+            const int dst = (wave * C::kLoadsPerTensor + i) * 1024;
+            load_lds16(kbase + off, ks + dst);
+            load_lds16(vbase + off, vs + dst);
+        }
+    };
+
+    issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
 
     // Q as the B operand: lane (query n, group hl) holds dims 16*kd + 8*hl .. +7.
     bf16x8 qreg[NQB][C::kKD];
@@ -84,150 +145,151 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     }
 
     f32x16 oacc[NQB][C::kMB];
-    float m_run[NQB], l_run[NQB];
+    float mref[NQB], lsum[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-        m_run[qb] = -INFINITY;
-        l_run[qb] = 0.0f;
+        mref[qb] = 0.0f;
+        lsum[qb] = 0.0f;
 #pragma unroll
         for (int mb = 0; mb < C::kMB; ++mb) oacc[qb][mb] = zero16();
     }
 
-    const int kv_end = min(T, q0 + C::kBM);            // keys 0 .. kv_end-1 are needed
-    const int ntiles = (kv_end + BN - 1) / BN;
-
-    // Cooperative tile loader: chunk c -> row c / (D/8), 16-byte column c % (D/8).
-    u32x4 kst[C::kPerThread], vst[C::kPerThread];
-    auto load_tile = [&](int j0) {
-#pragma unroll
-        for (int i = 0; i < C::kPerThread; ++i) {
-            const int c = tid + i * C::kThreads;
-            const int row = c / (D / 8), col = c % (D / 8);
-            const int key = j0 + row;
-            u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-            if (key < T) {
-                xk = load16(kbase + (size_t)key * kv_stride + col * 8);
-                xv = load16(vbase + (size_t)key * kv_stride + col * 8);
-            }
-            kst[i] = xk;
-            vst[i] = xv;
-        }
-    };
-    auto store_tile = [&](int buf) {
-        char* ks = smem + buf * C::kStage;
-        char* vs = ks + C::kKBytes;
-#pragma unroll
-        for (int i = 0; i < C::kPerThread; ++i) {
-            const int c = tid + i * C::kThreads;
-            const int row = c / (D / 8), col = c % (D / 8);
-            store16(ks + row * C::kKPitch + col * 16, kst[i]);
-            store16(vs + row * C::kVPitch + col * 16, vst[i]);
-        }
-    };
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    // Per-lane constants of the transposing V read (see cgqa_device.hpp): lane j of its
-    // 16-lane group points at row j/4 of a 4-row block and at column 4*(j%4) of the
-    // group's 16 dims (groups 1 and 3 take dims 16..31 of each 32-dim block).
-    const int tr_row = (lane & 15) >> 2;
-    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // Per-lane LDS offsets. K operand: row 32kb + n, logical chunk 2kd + hl. V operand
+    // (transposing read): lane j of its 16-lane group reads row 4*hl + j/4 (+8 for the
+    // second half) of a 16-row group, 8 bytes at logical column
+    // 32mb + 16*((lane>>4)&1) + 4*(j%4). Rows only enter the swizzle through r % 16,
+    // which does not depend on the block, so these are per-lane constants.
+    const int k_row_off = n * C::kRow;
+    const int k_swz = chunk_swizzle<D>(n);
+    const int v_r0 = 4 * hl + ((lane & 15) >> 2);
+    const int v_swz0 = chunk_swizzle<D>(v_r0), v_swz1 = chunk_swizzle<D>(v_r0 + 8);
+    const int v_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);   // + 4*mb
+    const int v_byte = 8 * (lane & 1);
 
     for (int jt = 0; jt < ntiles; ++jt) {
-        const int j0 = jt * BN;
-        if (jt + 1 < ntiles) load_tile(j0 + BN);
-        const char* ks = smem + (jt & 1) * C::kStage;
-        const char* vs = ks + C::kKBytes;
+        // Tile jt is complete once at most the next tile's loads are outstanding; the
+        // barrier also tells every wave that all waves are done with tile jt - 1,
+        // whose stage the loads of tile jt + 2 reuse.
+        if (jt + 1 < ntiles) wait_tiles_barrier<C::kLoadsPerTile>();
+        else wait_tiles_barrier<0>();
+        if (jt + 2 < ntiles) issue_tile(jt + 2);
 
-        if (qw + 32 * NQB - 1 >= j0) {   // some query of this wave sees some key here
-            // ---- S^T = K Q^T : rows are keys (A from LDS), columns are queries.
-            f32x16 s[C::kNKB][NQB];
+        const int j0 = jt * C::kBN;
+        const char* ks = smem + (jt % C::kStages) * C::kStage;
+        const char* vs = ks + C::kTile;
+
+        if (qw + 32 * NQB - 1 < j0) continue;   // every query of this wave is before the tile
 #pragma unroll
-            for (int kb = 0; kb < C::kNKB; ++kb) {
+        for (int kb = 0; kb < C::kNKB; ++kb) {
+            const int jb = j0 + 32 * kb;
+            if (qw + 32 * NQB - 1 < jb) break;      // the rest of the tile is masked
+            // S^T = K Q^T (rows: keys, A from LDS; columns: queries), masked above the
+            // diagonal. Register i of block qb is key jb + 8(i/4) + 4hl + i%4.
+            f32x16 s[NQB];
+            const bool need_mask = (jb + 31 > qw);
+            const char* krow = ks + 32 * kb * C::kRow + k_row_off;
+            auto scores = [&]() {
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = zero16();
+                for (int qb = 0; qb < NQB; ++qb) s[qb] = zero16();
 #pragma unroll
                 for (int kd = 0; kd < C::kKD; ++kd) {
-                    const bf16x8 ka = lds_read8(ks + (32 * kb + n) * C::kKPitch + (16 * kd + 8 * hl) * 2);
+                    const bf16x8 ka = lds_read8(krow + (((2 * kd + hl) ^ k_swz) << 4));
 #pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = mfma32x32x16(ka, qreg[qb][kd], s[kb][qb]);
+                    for (int qb = 0; qb < NQB; ++qb) s[qb] = mfma32x32x16(ka, qreg[qb][kd], s[qb]);
                 }
-            }
-            // ---- online softmax in log2 units, one query per lane.
-            const bool need_mask = (j0 + BN - 1 > qw);
+                if (need_mask) {
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-                const int query = qw + 32 * qb + n;
+                    for (int qb = 0; qb < NQB; ++qb) {
+                        const int rel = jb + 4 * hl - (qw + 32 * qb + n);   // key - query at i = 0
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            if (rel + 8 * (i >> 2) + (i & 3) > 0) s[qb][i] = -INFINITY;
+                    }
+                }
+            };
+            auto row_max = [&](int qb) {
                 float mx = -INFINITY;
 #pragma unroll
-                for (int kb = 0; kb < C::kNKB; ++kb) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        float x = s[kb][qb][i] * a.scale_log2;
-                        if (need_mask) {
-                            const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * hl + (i & 3);
-                            if (key > query) x = -INFINITY;
-                        }
-                        s[kb][qb][i] = x;
-                        mx = fmaxf(mx, x);
-                    }
-                }
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][i]);
                 mx = fmaxf(mx, swap_halves(mx));
-                const float m_new = fmaxf(m_run[qb], mx);   // finite: key 0 came first
-                const float alpha = exp2_fast(m_run[qb] - m_new);
-                float sum = 0.0f;
+                return mx * c;
+            };
+            float tsum[NQB];
+            auto exponentials = [&]() {
 #pragma unroll
-                for (int kb = 0; kb < C::kNKB; ++kb) {
+                for (int qb = 0; qb < NQB; ++qb) {
+                    tsum[qb] = 0.0f;
+                    const float nm = -mref[qb];
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const float p = exp2_fast(s[kb][qb][i] - m_new);
-                        s[kb][qb][i] = p;
-                        sum += p;
+                        const float p = exp2_fast(fmaf(s[qb][i], c, nm));
+                        s[qb][i] = p;
+                        tsum[qb] += p;
                     }
                 }
-                sum += swap_halves(sum);
-                l_run[qb] = l_run[qb] * alpha + sum;
-                m_run[qb] = m_new;
+            };
+
+            scores();
+            if (jb == 0) {
+                // Key 0 is in this block for every query: a finite reference max.
 #pragma unroll
-                for (int mb = 0; mb < C::kMB; ++mb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[qb][mb][i] *= alpha;
+                for (int qb = 0; qb < NQB; ++qb) mref[qb] = row_max(qb);
             }
-            // ---- O^T += V^T P^T, 16 keys per instruction. B = P straight from the score
-            // registers: registers 8t..8t+7 of a 32-key block hold keys
-            // 16t + 8*(s/4) + 4*hl + s%4 for slot s. A = the same keys of V, read
-            // transposed: slots 0..3 from rows 16t + 4*hl + r, slots 4..7 from rows
-            // 16t + 8 + 4*hl + r.
+            exponentials();
+            bool big = false;
 #pragma unroll
-            for (int kb = 0; kb < C::kNKB; ++kb) {
+            for (int qb = 0; qb < NQB; ++qb) big |= !(tsum[qb] <= kRescaleLimit);
+            if (wave_any(big)) {
+                // Rare: some score rose far above the reference. Recompute the block's
+                // scores, move the reference to the row max and rescale what was
+                // summed so far.
+                scores();
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    bf16x8 pb[NQB];
+                for (int qb = 0; qb < NQB; ++qb) {
+                    const float mnew = fmaxf(mref[qb], row_max(qb));
+                    const float alpha = exp2_fast(mref[qb] - mnew);
+                    mref[qb] = mnew;
+                    lsum[qb] *= alpha;
 #pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) pb[qb] = t == 0 ? pack_lo(s[kb][qb]) : pack_hi(s[kb][qb]);
-                    const int r0 = 32 * kb + 16 * t + 4 * hl + tr_row;
+                    for (int mb = 0; mb < C::kMB; ++mb)
 #pragma unroll
-                    for (int mb = 0; mb < C::kMB; ++mb) {
-                        const char* p0 = vs + r0 * C::kVPitch + (32 * mb + tr_col) * 2;
-                        const bf16x8 va = concat(lds_read_tr4(p0), lds_read_tr4(p0 + 8 * C::kVPitch));
+                        for (int i = 0; i < 16; ++i) oacc[qb][mb][i] *= alpha;
+                }
+                exponentials();
+            }
 #pragma unroll
-                        for (int qb = 0; qb < NQB; ++qb) oacc[qb][mb] = mfma32x32x16(va, pb[qb], oacc[qb][mb]);
-                    }
+            for (int qb = 0; qb < NQB; ++qb) lsum[qb] += tsum[qb];
+
+            // O^T += V^T P^T, 16 keys per instruction. B = P straight from the score
+            // registers: registers 8t..8t+7 hold keys 16t + 8*(s/4) + 4*hl + s%4 for
+            // slot s. A = the same keys of V, read transposed: slots 0..3 from rows
+            // 16t + 4*hl + r, slots 4..7 from rows 16t + 8 + 4*hl + r.
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                bf16x8 pb[NQB];
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) pb[qb] = t == 0 ? pack_lo(s[qb]) : pack_hi(s[qb]);
+                const char* vrow0 = vs + (32 * kb + 16 * t + v_r0) * C::kRow + v_byte;
+                const char* vrow1 = vrow0 + 8 * C::kRow;
+#pragma unroll
+                for (int mb = 0; mb < C::kMB; ++mb) {
+                    const int ch = 4 * mb + v_chunk;
+                    const bf16x8 va = concat(lds_read_tr4(vrow0 + ((ch ^ v_swz0) << 4)),
+                                             lds_read_tr4(vrow1 + ((ch ^ v_swz1) << 4)));
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb) oacc[qb][mb] = mfma32x32x16(va, pb[qb], oacc[qb][mb]);
                 }
             }
         }
-        if (jt + 1 < ntiles) store_tile((jt + 1) & 1);
-        __syncthreads();
     }
 
     // ---- epilogue: O = acc / l in bf16, LSE = ln2 * (m + log2 l).
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
         const int query = qw + 32 * qb + n;
+        const float l = lsum[qb] + swap_halves(lsum[qb]);
         if (query >= T) continue;
-        const float inv = 1.0f / l_run[qb];
+        const float inv = 1.0f / l;
         uint16_t* orow = a.o + ((size_t)b * T + query) * q_stride + (size_t)h * D;
 #pragma unroll
         for (int mb = 0; mb < C::kMB; ++mb) {
@@ -240,7 +302,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
                 *reinterpret_cast<u32x2*>(orow + 32 * mb + 8 * u + 4 * hl) = __builtin_bit_cast(u32x2, y);
             }
         }
-        if (hl == 0) a.lse[((size_t)b * Hq + h) * T + query] = (m_run[qb] + log2_fast(l_run[qb])) * kLn2;
+        if (hl == 0) a.lse[((size_t)b * Hq + h) * T + query] = (mref[qb] + log2_fast(l)) * kLn2;
     }
 }
 
@@ -250,14 +312,13 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     FwdArgs x = a;
     x.n_qtiles = (a.T + C::kBM - 1) / C::kBM;
     const long blocks = (long)x.n_qtiles * a.B * a.Hq;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NQB, BN, NW>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
-                       stream, x);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NQB, BN, NW>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, x);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     if (a.d == 64) return launch_fwd_t<64, 1, 64, 4>(a, stream);
-    return launch_fwd_t<128, 1, 64, 4>(a, stream);
+    return launch_fwd_t<128, 1, 32, 4>(a, stream);
 }
 
 }  // namespace cgqa

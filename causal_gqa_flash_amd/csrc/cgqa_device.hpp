@@ -114,6 +114,28 @@ __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_lo
 // Value held by the lane 32 positions away (the other k-group of the same column).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
+// True on every lane if `pred` holds on any active lane (a wave-uniform branch).
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane i's
+// 16 bytes from `src` land at `lds_base + 16 * i`; lds_base must be the same on every
+// lane. Completion is counted by vmcnt like any vector memory load, and the compiler
+// does not order later LDS reads after it: callers wait explicitly (wait_tiles).
+__device__ __forceinline__ void load_lds16(const uint16_t* src, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                     (void __attribute__((address_space(3)))*)lds_base, 16, 0, 0);
+}
+
+// Wait until at most N vector memory operations of this wave are outstanding and all
+// its LDS operations are done, then join the workgroup barrier. Unlike
+// __syncthreads() it leaves the newer (prefetch) loads in flight. The asm is also a
+// compiler memory barrier.
+template <int N>
+__device__ __forceinline__ void wait_tiles_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
