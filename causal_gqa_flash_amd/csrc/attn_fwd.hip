@@ -144,6 +144,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         }
     }
 
+    // Q in registers before the loop on every path, so the compiler's waits for it do
+    // not land inside the loop (where they would also wait for the tile prefetch).
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int kd = 0; kd < C::kKD; ++kd) asm volatile("" ::"v"(qreg[qb][kd]));
+
     f32x16 oacc[NQB][C::kMB];
     float mref[NQB], lsum[NQB];
 #pragma unroll

@@ -114,16 +114,33 @@ __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_lo
 // Value held by the lane 32 positions away (the other k-group of the same column).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
+// Instruction-scheduling hints for a basic block (groups are filled in order).
+constexpr int kSchedVALU = 0x002;
+constexpr int kSchedMFMA = 0x008;
+constexpr int kSchedDSRead = 0x100;
+#define CGQA_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
 // True on every lane if `pred` holds on any active lane (a wave-uniform branch).
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane i's
-// 16 bytes from `src` land at `lds_base + 16 * i`; lds_base must be the same on every
-// lane. Completion is counted by vmcnt like any vector memory load, and the compiler
-// does not order later LDS reads after it: callers wait explicitly (wait_tiles).
-__device__ __forceinline__ void load_lds16(const uint16_t* src, void* lds_base) {
-    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                     (void __attribute__((address_space(3)))*)lds_base, 16, 0, 0);
+// 16 bytes from `src` land at LDS byte address `lds_base + 16 * i` (M0 holds the
+// base, which must be the same on every lane). Completion is counted by vmcnt like any
+// vector memory load. The instruction is issued from inline asm so that the compiler
+// does not treat every later LDS read as dependent on it (it would wait for all loads
+// in flight, including the prefetch); callers order it with wait_tiles_barrier. For
+// the compiler's own vmcnt bookkeeping the extra loads only make its waits longer,
+// never shorter, since loads complete in order.
+__device__ __forceinline__ void load_lds16(const uint16_t* src, const void* lds_base) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
+    // M0 is reserved by the compiler, so the asm restores the value it found.
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(m0)
+        : "memory");
 }
 
 // Wait until at most N vector memory operations of this wave are outstanding and all
