@@ -1,11 +1,12 @@
 // Forward kernel of causal grouped-query flash attention for gfx950.
 //
 // Method (page "A transformer in PTX", section "Flash attention"): one workgroup owns
-// a block of queries of one head and walks the key blocks up to the diagonal. The
-// score matrix is never written to memory: each query keeps a running reference max m
-// and sum l (online softmax) in log2 units, the scores being multiplied once by
-// scale * log2(e) and each probability being 2^(s - m). At the end O = acc / l and the
-// row's log-sum-exp, converted to natural log, is saved for the backward.
+// a block of queries of one head and visits the key blocks from the first one to the
+// block holding the diagonal. Scores never go to memory: each query carries a
+// reference max m and a sum l (online softmax) in base-2 units, the scores being
+// scaled a single time by scale * log2(e) and each probability being 2^(s - m). At the
+// end O = acc / l, and the row's log-sum-exp, converted to natural log, is stored for
+// the backward.
 //
 // gfx950 design (not the page's sm_120 one):
 //  * The scores are computed transposed, S^T = K Q^T, on the 32x32x16 bf16 matrix

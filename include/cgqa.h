@@ -2,14 +2,14 @@
  * cgqa: causal grouped-query flash attention for AMD MI355X (gfx950).
  *
  * The operation is the causal softmax attention of a Llama-style decoder with
- * grouped-query heads (page "A transformer in PTX", section "The model": several query
- * heads share one key/value head), computed as flash attention (section "Flash
- * attention": the T x T score matrix is never written out; each row keeps a running
- * max and sum in log2 units; the forward saves each row's log-sum-exp so the backward
- * can recompute the probabilities), with a two-kernel deterministic backward (section
- * "The same bits every time": dQ per block of queries; dK/dV per block of keys looping
- * over the query heads that share the key/value head; no float atomics, so two runs
- * give identical bits).
+ * grouped-query heads (page "A transformer in PTX", section "The model": groups of query
+ * heads read one shared key/value head), computed as flash attention (section "Flash
+ * attention": scores never go to memory; each row carries a running max and sum in
+ * base-2 units; the forward stores each row's log-sum-exp so the backward can rebuild
+ * the probabilities), with a deterministic two-kernel backward (section "The same bits
+ * every time": one kernel owns blocks of queries and produces dQ, the other owns blocks
+ * of keys and produces dK/dV, visiting every query head of the key/value head's group;
+ * no float atomics, so repeated runs are bit-identical).
  *
  * Shapes and layout (all tensors contiguous, row-major, owned by the caller):
  *   q, o, dO : [B][T][Hq][d]   bfloat16 (passed as uint16_t bit patterns)
@@ -62,8 +62,8 @@ int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
              uint16_t* o, float* lse,
              int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
 
-/* Backward, query side (section "The same bits every time": one owner per block of
- * queries). For the loss L = sum(O * dO): recomputes P from q, k and lse, writes
+/* Backward, query side (section "The same bits every time": each block of queries
+ * has a single owning workgroup). For the loss L = sum(O * dO): recomputes P from q, k and lse, writes
  * delta = rowsum(dO * o) (from the bf16 o given) and dq = dL/dq.
  * Reads q, k, v, o, dO, lse; overwrites delta and dq. */
 int attn_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -71,9 +71,9 @@ int attn_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 float* delta, float* dq,
                 int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
 
-/* Backward, key side (same section: one owner per block of keys, looping over the
- * query heads that share its key/value head in ascending order, then over query
- * blocks in ascending order). Writes dk = dL/dk and dv = dL/dv, summed over the
+/* Backward, key side (same section: each block of keys has a single owning workgroup,
+ * which visits the query heads of its key/value head's group in ascending order and,
+ * for each, the query blocks in ascending order). Writes dk = dL/dk and dv = dL/dv, summed over the
  * group. Reads the delta written by attn_bwd_dq, so it must be enqueued after that
  * call on the same stream (or after an event recorded behind it).
  * Reads q, k, v, dO, lse, delta; overwrites dk and dv. */

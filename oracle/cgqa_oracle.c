@@ -8,25 +8,25 @@
  *
  * What it computes is the plain definition of the method, not the method's blocked
  * algorithm. Flash attention is an exact reordering of softmax attention (page "A
- * transformer in PTX", section "Flash attention": the naive kernels write out the
- * whole T x T score matrix for every head; the flash kernel produces the same result
- * with an online softmax). So this file writes out the whole score matrix for each
- * (batch, query head), exactly like the naive kernels, in double precision, with no
- * blocking, no online softmax and no log2 units.
+ * transformer in PTX", section "Flash attention", contrasts it with naive kernels that
+ * store every score of a head; both give the same result). So this file stores the
+ * full score matrix of each (batch, query head), as the naive kernels do, in double
+ * precision, with no blocking, no online softmax and no log2 units.
  *
  * Conventions (readings of the pages, each one stated where it is used):
  *  - Layout: q, o, dO, dq are [B][T][Hq][d]; k, v, dk, dv are [B][T][Hkv][d];
  *    lse and delta are [B][Hq][T]. Element (b,t,h,c) of a [B][T][H][d] tensor sits
  *    at ((b*T + t)*H + h)*d + c.
- *  - Grouped-query sharing ("A transformer in PTX", section "The model": 6 query heads
- *    share 2 key/value heads): query head h reads key/value head h / G, G = Hq / Hkv,
- *    i.e. contiguous groups of G query heads.
- *  - Causality (section "Flash attention": key blocks are walked up to the diagonal):
- *    query i sees keys 0..i inclusive; query and key positions share one index.
- *  - Scale: scores are q.k * scale (the pages multiply by 1/sqrt(64) once).
+ *  - Grouped-query sharing ("A transformer in PTX", section "The model": the dev preset
+ *    maps six query heads onto two key/value heads): query head h reads key/value head
+ *    h / G, G = Hq / Hkv, i.e. contiguous groups of G query heads.
+ *  - Causality (section "Flash attention": a query block only visits key blocks that
+ *    are not past it): query i sees keys 0..i inclusive; queries and keys share one
+ *    position index.
+ *  - Scale: scores are q.k * scale (the pages apply 1/sqrt(64) a single time).
  *  - LSE is the natural-log log-sum-exp of each row's scaled scores (section "Flash
- *    attention": the forward saves each row's log-sum-exp so the backward can
- *    recompute the probabilities).
+ *    attention": the forward keeps it so that the backward can rebuild the
+ *    probabilities without storing them).
  *  - Backward: the vector-Jacobian product for the loss L = sum(O * dO), with
  *    D_i = sum_c dO_ic O_ic. dK and dV of a key/value head sum over the G query
  *    heads that share it (section "The same bits every time": the dK/dV kernel loops

@@ -4,8 +4,8 @@ This module is shared by the CPU oracle's tests and the HIP path's tests and ben
 It holds none of the attention arithmetic: it only draws normal samples and rounds
 them to bfloat16 bit patterns.
 
-Workloads (sizes of the page "A transformer in PTX", section "The model": 6 query
-heads of 64 share 2 key/value heads in the dev preset, plus larger shapes):
+Workloads (sizes after the page "A transformer in PTX", section "The model", whose dev
+preset maps six 64-wide query heads onto two key/value heads, plus larger shapes):
 every input is drawn N(0, 1) in float32 with numpy's PCG64 ``default_rng(seed)`` in
 the order Q, K, V, dO, optionally multiplied by a constant (2 for Q and K in the
 "peaky" workload, exact in bf16), then rounded to bf16 by round-to-nearest-even.
