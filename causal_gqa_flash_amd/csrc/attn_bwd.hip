@@ -250,51 +250,80 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------- dK/dV kernel
-template <int D, int BQ, int NW>
+// One workgroup owns NKW blocks of 32 keys of one key/value head. Its waves form HS
+// head slots of NKW waves: slot s handles the query heads s, s + HS, ... of the group
+// (ascending), each wave of a slot one key block, and the waves of a slot share staged
+// Q/dO tiles of their current head. All slots step through the query tiles together,
+// from the tile holding the workgroup's earliest key to the last. At the end the slots'
+// partial dK and dV of each key are summed through LDS in ascending slot order: every
+// output element still has one writer and a fixed summation order.
+// Which key blocks a workgroup gets: the causal work of block kb falls with kb (it
+// meets T - 32kb queries). When the grid is several rounds deep, consecutive blocks
+// per workgroup with the early (heavy) ones launched first balance well. When it is a
+// single round, the blocks are dealt in zig-zag order (0, last, 1, last-1, ...) so every
+// workgroup gets early and late blocks and about the same work; a wave's block is then
+// rotated by its slot so that the waves sharing a SIMD mix early and late blocks.
+template <int D, int BQ, int NKW, int HS>
 struct DkvCfg {
-    static constexpr int kThreads = NW * 64;
-    static constexpr int kBN = NW * 32;            // keys per workgroup (32 per wave)
+    static constexpr int kThreads = NKW * HS * 64;
+    static constexpr int kBN = NKW * 32;           // keys per workgroup (32 per wave)
     static constexpr int kKD = D / 16;
     static constexpr int kMB = D / 32;
     static constexpr int kQSB = BQ / 32;           // 32-query blocks per staged tile
     static constexpr int kPitch = D * 2 + 16;      // Q and dO rows in LDS (fp16)
     static constexpr int kTile = BQ * kPitch;
     static constexpr int kStage = 2 * kTile + 2 * BQ * 4;   // Q, dO, lse2, delta
-    static constexpr int kLds = 2 * kStage;
+    static constexpr int kSlot = 2 * kStage;                // double buffered
+    static constexpr int kSlotThreads = NKW * 64;
     static constexpr int kChunks = BQ * D / 8;
-    static constexpr int kPerThread = kChunks / kThreads;
+    static constexpr int kPerThread = kChunks / kSlotThreads;
+    // Reduction area: one 32-dim accumulator block (16 floats) per lane of every wave
+    // of slots 1 .. HS-1; the blocks are reduced one after another.
+    static constexpr int kRedBytes = NKW * (HS - 1) * 64 * 16 * 4;
+    static constexpr int kLds = (HS * kSlot > kRedBytes) ? HS * kSlot : kRedBytes;
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(BQ % 32 == 0, "query tile");
-    static_assert(kChunks % kThreads == 0, "tile load must split evenly over the threads");
-    static_assert(2 * BQ <= kThreads, "one thread per staged lse / delta value");
+    static_assert(kChunks % kSlotThreads == 0, "tile load must split evenly over a slot");
+    static_assert(2 * BQ <= kSlotThreads, "one thread per staged lse / delta value");
+    static_assert(kThreads <= 1024, "workgroup size");
     static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
-template <int D, int BQ, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a) {
-    using C = DkvCfg<D, BQ, NW>;
+template <int D, int BQ, int NKW, int HS>
+__global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) {
+    using C = DkvCfg<D, BQ, NKW, HS>;
     __shared__ __attribute__((aligned(16))) char smem[C::kLds];
 
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
     const int G = Hq / Hkv;
     const int bg_count = a.B * Hkv;
     const int bid = blockIdx.x;
-    const int kt = bid / bg_count;                 // key block 0 (the most queries) first
+    const int kt = bid / bg_count;                 // which group of zig-zag positions
     const int bg = bid % bg_count;
     const int b = bg / Hkv, g = bg % Hkv;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    const int hs = wave / NKW;                     // head slot
+    const int pos = (wave + hs) % NKW;             // key-block position within the workgroup
+    const int stid = tid % C::kSlotThreads;        // thread index within the slot
     const int n = lane & 31, hl = lane >> 5;
-    const int k0 = kt * C::kBN;
-    const int kw = k0 + wave * 32;                 // first key of this wave
-    const int key = kw + n;                        // this lane's key (column)
+    // Workgroup kt takes positions NKW*kt .. NKW*kt + NKW - 1 of the block order: the
+    // identity, or zig-zag (position p holds block p/2 for even p, nkb - 1 - p/2 for
+    // odd p). Either way its earliest block sits at its first position.
+    const int nkb = (T + 31) / 32;
+    auto block_at = [&](int p) { return !a.zigzag ? p : (p & 1) ? nkb - 1 - (p >> 1) : (p >> 1); };
+    const int p0 = NKW * kt;
+    const int kb_first = p0 < nkb ? block_at(p0) : nkb;   // the workgroup's earliest block
+    const int gp = p0 + pos;
+    const int kwb = gp < nkb ? 32 * block_at(gp) : T;     // first key of this wave (T: none)
+    const int key = kwb + n;                       // this lane's key (column)
 
     const size_t q_stride = (size_t)Hq * D;
     const size_t kv_stride = (size_t)Hkv * D;
     const size_t kvoff = ((size_t)b * T * Hkv + g) * D;
 
-    // K and V of the lane's key as B operands (dims 16*kd + 8*hl .. +7).
+    // K and V of the lane's key as B operands (dims 16*kd + 8*hl .. +7), in fp16.
     f16x8 kreg[C::kKD], vreg[C::kKD];
 #pragma unroll
     for (int kd = 0; kd < C::kKD; ++kd) {
@@ -312,23 +341,26 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
     for (int mb = 0; mb < C::kMB; ++mb) { dkacc[mb] = zero16(); dvacc[mb] = zero16(); }
 
-    // Steps: heads of the group ascending, then query tiles ascending from the one
-    // holding the first key of this workgroup.
+    // Steps of a slot: its heads ascending, then query tiles ascending from the tile
+    // holding the workgroup's earliest key. Every slot has the same number of steps
+    // (HS divides G).
     const int nqt = (T + BQ - 1) / BQ;
-    const int qt_begin = k0 / BQ;
+    const int qt_begin = (32 * kb_first) / BQ;
     const int per_head = nqt - qt_begin;
-    const int nsteps = k0 < T ? G * per_head : 0;
+    const int heads_per_slot = G / HS;
+    const int nsteps = kb_first < nkb ? heads_per_slot * per_head : 0;
 
+    char* slot_base = smem + hs * C::kSlot;
     u32x4 qst[C::kPerThread], dst[C::kPerThread];
     float lst = 0.0f;
     auto load_step = [&](int step) {
-        const int h = g * G + step / per_head;
+        const int h = g * G + hs + HS * (step / per_head);
         const int qs0 = (qt_begin + step % per_head) * BQ;
         const size_t hoff = ((size_t)b * T * Hq + h) * D;
 #pragma unroll
         for (int i = 0; i < C::kPerThread; ++i) {
-            const int c = tid + i * C::kThreads;
-            const int row = c / (D / 8), col = c % (D / 8);
+            const int ch = stid + i * C::kSlotThreads;
+            const int row = ch / (D / 8), col = ch % (D / 8);
             const int query = qs0 + row;
             u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u};
             if (query < T) {
@@ -339,25 +371,25 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a) {
             qst[i] = xq;
             dst[i] = xd;
         }
-        if (tid < 2 * BQ) {
-            const int query = qs0 + (tid % BQ);
+        if (stid < 2 * BQ) {
+            const int query = qs0 + (stid % BQ);
             const size_t off = ((size_t)b * Hq + h) * T + query;
-            if (tid < BQ) lst = query < T ? a.lse[off] * kLog2e : INFINITY;   // P = 0 past T
+            if (stid < BQ) lst = query < T ? a.lse[off] * kLog2e : INFINITY;   // P = 0 past T
             else lst = query < T ? a.delta[off] : 0.0f;
         }
     };
     auto store_step = [&](int buf) {
-        char* qs = smem + buf * C::kStage;
+        char* qs = slot_base + buf * C::kStage;
         char* ds = qs + C::kTile;
         float* ls = reinterpret_cast<float*>(ds + C::kTile);
 #pragma unroll
         for (int i = 0; i < C::kPerThread; ++i) {
-            const int c = tid + i * C::kThreads;
-            const int row = c / (D / 8), col = c % (D / 8);
+            const int ch = stid + i * C::kSlotThreads;
+            const int row = ch / (D / 8), col = ch % (D / 8);
             store16(qs + row * C::kPitch + col * 16, bf16x8_to_f16_bits(qst[i]));
             store16(ds + row * C::kPitch + col * 16, bf16x8_to_f16_bits(dst[i]));
         }
-        if (tid < 2 * BQ) ls[tid] = lst;
+        if (stid < 2 * BQ) ls[stid] = lst;
     };
 
     if (nsteps > 0) {
@@ -371,7 +403,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a) {
 
     for (int step = 0; step < nsteps; ++step) {
         if (step + 1 < nsteps) load_step(step + 1);
-        const char* qs = smem + (step & 1) * C::kStage;
+        const char* qs = slot_base + (step & 1) * C::kStage;
         const char* ds = qs + C::kTile;
         const float* lse2s = reinterpret_cast<const float*>(ds + C::kTile);
         const float* dels = lse2s + BQ;
@@ -380,7 +412,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
         for (int sb = 0; sb < C::kQSB; ++sb) {
             const int qb0 = qs0 + 32 * sb;             // first query of this block
-            if (qb0 + 31 < kw) continue;               // every query precedes every key
+            if (qb0 + 31 < kwb) continue;              // every query precedes every key
             f32x16 s = zero16(), dp = zero16();
 #pragma unroll
             for (int kd = 0; kd < C::kKD; ++kd) {
@@ -389,7 +421,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a) {
                 dp = mfma32x32x16(lds_read8_f16(ds + off), vreg[kd], dp);
             }
             // Register i holds query qb0 + 8*(i/4) + 4*hl + i%4 of the lane's key.
-            const bool need_mask = (qb0 < kw + 31);
+            const bool need_mask = (qb0 < kwb + 31);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int r = 32 * sb + 8 * u + 4 * hl;
@@ -424,23 +456,53 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkv_kernel(BwdArgs a) {
         __syncthreads();
     }
 
-    if (key < T) {
-        float* dkrow = a.dk + kvoff + (size_t)key * kv_stride;
-        float* dvrow = a.dv + kvoff + (size_t)key * kv_stride;
+    // ---- sum the head slots (ascending) and store: one 32-dim block of dK, then of dV,
+    // at a time through the same LDS area; every wave's lane values line up across
+    // slots.
+    float* red = reinterpret_cast<float*>(smem);
+    auto reduce_store = [&](f32x16 (&acc)[C::kMB], float* out, float mul) {
 #pragma unroll
-        for (int mb = 0; mb < C::kMB; ++mb)
+        for (int mb = 0; mb < C::kMB; ++mb) {
+            if (HS > 1) {
+                if (hs > 0) {
+                    float* mine = red + (size_t)(((hs - 1) * NKW + pos) * 64 + lane) * 16;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                f32x4 xk, xv;
+                    for (int u = 0; u < 4; ++u) {
+                        f32x4 x;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    xk[r] = dkacc[mb][4 * u + r] * a.scale;
-                    xv[r] = dvacc[mb][4 * u + r];
+                        for (int r = 0; r < 4; ++r) x[r] = acc[mb][4 * u + r];
+                        *reinterpret_cast<f32x4*>(mine + 4 * u) = x;
+                    }
                 }
-                *reinterpret_cast<f32x4*>(dkrow + 32 * mb + 8 * u + 4 * hl) = xk;
-                *reinterpret_cast<f32x4*>(dvrow + 32 * mb + 8 * u + 4 * hl) = xv;
+                __syncthreads();
+                if (hs == 0) {
+#pragma unroll
+                    for (int s2 = 1; s2 < HS; ++s2) {
+                        const float* src = red + (size_t)(((s2 - 1) * NKW + pos) * 64 + lane) * 16;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * u);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) acc[mb][4 * u + r] += x[r];
+                        }
+                    }
+                }
+                __syncthreads();
             }
-    }
+            if (hs == 0 && key < T) {
+                float* row = out + kvoff + (size_t)key * kv_stride;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    f32x4 x;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) x[r] = acc[mb][4 * u + r] * mul;
+                    *reinterpret_cast<f32x4*>(row + 32 * mb + 8 * u + 4 * hl) = x;
+                }
+            }
+        }
+    };
+    reduce_store(dkacc, a.dk, a.scale);
+    reduce_store(dvacc, a.dv, 1.0f);
 }
 
 template <int D, int NQB, int BN, int NW>
@@ -454,13 +516,15 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, int BQ, int NW>
+template <int D, int BQ, int NKW, int HS>
 static hipError_t launch_dkv_t(const BwdArgs& a, hipStream_t stream) {
-    using C = DkvCfg<D, BQ, NW>;
+    using C = DkvCfg<D, BQ, NKW, HS>;
     BwdArgs x = a;
-    x.n_tiles = (a.T + C::kBN - 1) / C::kBN;
+    x.n_tiles = ((a.T + 31) / 32 + NKW - 1) / NKW;
     const long blocks = (long)x.n_tiles * a.B * a.Hkv;
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NW>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
+    // One workgroup per CU fits (LDS and registers); gfx950 parts have 256 CUs.
+    x.zigzag = blocks <= 256 ? 1 : 0;
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
                        stream, x);
     return hipGetLastError();
 }
@@ -470,9 +534,19 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
     return launch_dq_t<128, 1, 32, 4>(a, stream);
 }
 
+// Head slots: as many as divide the group size and fit. A slot stages its own Q/dO
+// tiles, and a workgroup of W waves keeps W/4 waves per SIMD, so the register budget of
+// a wave bounds W: d=64 keeps up to 12 waves. A d=128 wave already needs all 256 VGPRs
+// (extra slots spill), so d=128 uses one slot.
 hipError_t launch_bwd_dkv(const BwdArgs& a, hipStream_t stream) {
-    if (a.d == 64) return launch_dkv_t<64, 64, 4>(a, stream);
-    return launch_dkv_t<128, 64, 4>(a, stream);
+    const int G = a.Hq / a.Hkv;
+    if (a.d == 64) {
+        if (G % 4 == 0) return launch_dkv_t<64, 64, 2, 4>(a, stream);
+        if (G % 3 == 0) return launch_dkv_t<64, 32, 4, 3>(a, stream);
+        if (G % 2 == 0) return launch_dkv_t<64, 64, 4, 2>(a, stream);
+        return launch_dkv_t<64, 64, 4, 1>(a, stream);
+    }
+    return launch_dkv_t<128, 32, 4, 1>(a, stream);
 }
 
 }  // namespace cgqa

@@ -32,6 +32,7 @@ struct BwdArgs {
     float scale;        // softmax scale (dS carries it into dQ and dK)
     float scale_log2;   // scale * log2(e)
     int n_tiles;        // set by the launcher
+    int zigzag;         // dK/dV: deal key blocks in zig-zag order (set by the launcher)
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
