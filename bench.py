@@ -54,6 +54,70 @@ def measured_traffic(kernel):
     return None if k is None else k.get("bytes_per_launch")
 
 
+COPY_BYTES = 256 << 20   # calibration copy: 256 MiB read and 256 MiB written
+
+
+def pmc_workload(args):
+    """A short run for rocprofv3 --pmc: each kernel a few times, then a plain device copy
+    of COPY_BYTES (torch's copy kernel) whose FETCH_SIZE / WRITE_SIZE calibrate the
+    counters to bytes."""
+    import numpy as np
+    import torch
+    import causal_gqa_flash_amd as cg
+    import synthetic_inputs as si
+    w = si.WORKLOAD_BY_NAME[WORKLOAD]
+    x = si.make_workload_inputs(w, seed=3)
+    dev = {n: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for n, a in x.items()}
+    for _ in range(args.steps):
+        o, lse = cg.attn_fwd(dev["q"], dev["k"], dev["v"], scale=w.scale)
+        delta, dq = cg.attn_bwd_dq(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, scale=w.scale)
+        cg.attn_bwd_dkv(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, scale=w.scale)
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_workload": w.name, "steps": args.steps, "copy_bytes": COPY_BYTES}), flush=True)
+
+
+def pmc_summarize(fetch_dir, write_dir, out_path):
+    """Per-launch HBM bytes of each kernel from two rocprofv3 --pmc runs of
+    pmc_workload (FETCH_SIZE, then WRITE_SIZE), scaled by what the same counters read
+    for the calibration copy (COPY_BYTES each way)."""
+    import csv
+    import glob
+
+    def read(d, counter):
+        path = glob.glob(os.path.join(d, "*counter_collection.csv"))[0]
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        return per
+
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = read(d, counter)
+        copy = [v for (i, name), v in per.items() if "copy" in name.lower() or "elementwise" in name.lower()]
+        if not copy:
+            raise SystemExit(f"no copy kernel found in {d}")
+        factor = COPY_BYTES / (max(copy) * 1024.0)     # counter is in KiB
+        for kern in ("attn_fwd", "attn_bwd_dq", "attn_bwd_dkv"):
+            vals = [v for (i, name), v in per.items() if kern + "_kernel" in name]
+            if vals:
+                kb = sum(vals) / len(vals)
+                res.setdefault(kern, {})[counter] = {"kib_per_dispatch": round(kb, 1), "calibration": round(factor, 4),
+                                                     "bytes": kb * 1024.0 * factor}
+    out = {"workload": WORKLOAD, "kernel_source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES,
+           "kernels": {k: {"bytes_per_launch": round(v["FETCH_SIZE"]["bytes"] + v["WRITE_SIZE"]["bytes"]),
+                           "fetch": v["FETCH_SIZE"], "write": v["WRITE_SIZE"]} for k, v in res.items()}}
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(w, x, budget_s):
     """The fp64 CPU oracle (as it is) on whole (batch, kv head) slices of the workload,
     forward and backward, until about budget_s seconds have passed."""
@@ -87,11 +151,22 @@ def main():
     ap.add_argument("--repeats", type=int, default=5, help="timed repeats; the median is reported")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="run the short workload that rocprofv3 --pmc profiles (see profiles/)")
+    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output folders into the traffic summary")
     args = ap.parse_args()
+    if args.pmc_summarize:
+        pmc_summarize(args.pmc_summarize[0], args.pmc_summarize[1], TRAFFIC_FILE)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs on a single MI355X and has no "
               f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.pmc_workload:
+        pmc_workload(args)
+        return
 
     import numpy as np
     import torch

@@ -263,49 +263,60 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 // single round, the blocks are dealt in zig-zag order (0, last, 1, last-1, ...) so every
 // workgroup gets early and late blocks and about the same work; a wave's block is then
 // rotated by its slot so that the waves sharing a SIMD mix early and late blocks.
-template <int D, int BQ, int NKW, int HS>
+template <int D, int BQ, int NKW, int HS, int NR>
 struct DkvCfg {
     static constexpr int kThreads = NKW * HS * 64;
-    static constexpr int kBN = NKW * 32;           // keys per workgroup (32 per wave)
     static constexpr int kKD = D / 16;
     static constexpr int kMB = D / 32;
     static constexpr int kQSB = BQ / 32;           // 32-query blocks per staged tile
-    static constexpr int kPitch = D * 2 + 16;      // Q and dO rows in LDS (fp16)
+    // Raw ring (NR stages, filled by DMA two steps ahead when NR = 3): Q and dO rows as
+    // bf16, then lse and delta as fp32.
+    static constexpr int kRawRow = D * 2;
+    static constexpr int kRawTile = BQ * kRawRow;
+    static constexpr int kRawStage = 2 * kRawTile + 2 * BQ * 4;
+    // Converted double buffer: Q and dO rows as fp16 (padded pitch), lse * log2(e)
+    // (+inf past T) and delta (0 past T).
+    static constexpr int kPitch = D * 2 + 16;
     static constexpr int kTile = BQ * kPitch;
-    static constexpr int kStage = 2 * kTile + 2 * BQ * 4;   // Q, dO, lse2, delta
-    static constexpr int kSlot = 2 * kStage;                // double buffered
+    static constexpr int kConvStage = 2 * kTile + 2 * BQ * 4;
+    static constexpr int kSlot = NR * kRawStage + 2 * kConvStage;
     static constexpr int kSlotThreads = NKW * 64;
-    static constexpr int kChunks = BQ * D / 8;
-    static constexpr int kPerThread = kChunks / kSlotThreads;
+    static constexpr int kTileLoads = kRawTile / 1024 / NKW;     // per tensor, per wave
+    static constexpr int kStatLanes = 2 * BQ / NKW;              // 4-byte DMA lanes per wave
+    static constexpr int kVmPerStep = 2 * kTileLoads + 1;        // DMA instructions per wave
+    static constexpr int kConvChunks = kRawTile / 16 / kSlotThreads;   // per tensor, per thread
     // Reduction area: one 32-dim accumulator block (16 floats) per lane of every wave
     // of slots 1 .. HS-1; the blocks are reduced one after another.
     static constexpr int kRedBytes = NKW * (HS - 1) * 64 * 16 * 4;
     static constexpr int kLds = (HS * kSlot > kRedBytes) ? HS * kSlot : kRedBytes;
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(BQ % 32 == 0, "query tile");
-    static_assert(kChunks % kSlotThreads == 0, "tile load must split evenly over a slot");
-    static_assert(2 * BQ <= kSlotThreads, "one thread per staged lse / delta value");
+    static_assert(NR == 2 || NR == 3, "raw ring depth");
+    static_assert(kRawTile % (1024 * NKW) == 0, "tile DMA must split evenly over a slot");
+    static_assert(kStatLanes >= 1 && kStatLanes <= 64 && (2 * BQ) % NKW == 0, "stat DMA lanes");
+    static_assert(kRawTile % (16 * kSlotThreads) == 0, "conversion must split evenly");
     static_assert(kThreads <= 1024, "workgroup size");
     static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
-template <int D, int BQ, int NKW, int HS>
+template <int D, int BQ, int NKW, int HS, int NR>
 __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) {
-    using C = DkvCfg<D, BQ, NKW, HS>;
-    __shared__ __attribute__((aligned(16))) char smem[C::kLds];
+    using C = DkvCfg<D, BQ, NKW, HS, NR>;
+    __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
 
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
     const int G = Hq / Hkv;
     const int bg_count = a.B * Hkv;
     const int bid = blockIdx.x;
-    const int kt = bid / bg_count;                 // which group of zig-zag positions
+    const int kt = bid / bg_count;                 // which group of block positions
     const int bg = bid % bg_count;
     const int b = bg / Hkv, g = bg % Hkv;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int hs = wave / NKW;                     // head slot
-    const int pos = (wave + hs) % NKW;             // key-block position within the workgroup
+    const int kwr = wave % NKW;                    // wave index within the slot
+    const int pos = (kwr + hs) % NKW;              // key-block position within the workgroup
     const int stid = tid % C::kSlotThreads;        // thread index within the slot
     const int n = lane & 31, hl = lane >> 5;
     // Workgroup kt takes positions NKW*kt .. NKW*kt + NKW - 1 of the block order: the
@@ -337,6 +348,12 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
         vreg[kd] = bf16x8_to_f16(xv);
     }
 
+    // K and V in registers before the loop on every path, so the compiler's waits for
+    // them stay out of the loop (there they would also wait for the DMA prefetch, which
+    // the compiler does not track).
+#pragma unroll
+    for (int kd = 0; kd < C::kKD; ++kd) asm volatile("" ::"v"(kreg[kd]), "v"(vreg[kd]));
+
     f32x16 dkacc[C::kMB], dvacc[C::kMB];
 #pragma unroll
     for (int mb = 0; mb < C::kMB; ++mb) { dkacc[mb] = zero16(); dvacc[mb] = zero16(); }
@@ -351,63 +368,88 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     const int nsteps = kb_first < nkb ? heads_per_slot * per_head : 0;
 
     char* slot_base = smem + hs * C::kSlot;
-    u32x4 qst[C::kPerThread], dst[C::kPerThread];
-    float lst = 0.0f;
-    auto load_step = [&](int step) {
-        const int h = g * G + hs + HS * (step / per_head);
-        const int qs0 = (qt_begin + step % per_head) * BQ;
+    auto raw_stage = [&](int st) { return slot_base + (st % NR) * C::kRawStage; };
+    auto conv_stage = [&](int st) { return slot_base + NR * C::kRawStage + (st & 1) * C::kConvStage; };
+    auto step_head = [&](int st) { return g * G + hs + HS * (st / per_head); };
+    auto step_q0 = [&](int st) { return (qt_begin + st % per_head) * BQ; };
+
+    // DMA of one step into the raw ring: each wave of the slot copies kTileLoads KB of
+    // Q rows and of dO rows (row-major, 1 KB per instruction), and kStatLanes floats of
+    // lse / delta (4 bytes per lane). Query rows past T read row T-1; the conversion
+    // masks them.
+    auto issue_step = [&](int st) {
+        char* raw = raw_stage(st);
+        const int h = step_head(st);
+        const int qs0 = step_q0(st);
         const size_t hoff = ((size_t)b * T * Hq + h) * D;
 #pragma unroll
-        for (int i = 0; i < C::kPerThread; ++i) {
-            const int ch = stid + i * C::kSlotThreads;
-            const int row = ch / (D / 8), col = ch % (D / 8);
-            const int query = qs0 + row;
-            u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u};
-            if (query < T) {
-                const size_t off = hoff + (size_t)query * q_stride + col * 8;
-                xq = load16(a.q + off);
-                xd = load16(a.dO + off);
+        for (int i = 0; i < C::kTileLoads; ++i) {
+            const int ci = kwr * C::kTileLoads + i;              // 1 KB chunk of the tile
+            const int byte = ci * 1024 + 16 * lane;
+            const int row = byte / C::kRawRow, col = (byte % C::kRawRow) / 16;
+            const int query = min(qs0 + row, T - 1);
+            const size_t off = hoff + (size_t)query * q_stride + col * 8;
+            load_lds16(a.q + off, raw + ci * 1024);
+            load_lds16(a.dO + off, raw + C::kRawTile + ci * 1024);
+        }
+        if (lane < C::kStatLanes) {
+            const int f = kwr * C::kStatLanes + lane;            // float index in lse|delta
+            const int query = min(qs0 + (f % BQ), T - 1);
+            const float* src = (f < BQ ? a.lse : a.delta) + ((size_t)b * Hq + h) * T + query;
+            load_lds4(src, raw + 2 * C::kRawTile + kwr * C::kStatLanes * 4);
+        }
+    };
+    // Raw step -> converted step (fp16 rows, scaled and masked statistics).
+    auto convert_step = [&](int st) {
+        const char* raw = raw_stage(st);
+        char* cv = conv_stage(st);
+        const int qs0 = step_q0(st);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int i = 0; i < C::kConvChunks; ++i) {
+                const int ch = stid + i * C::kSlotThreads;
+                const int row = ch / (C::kRawRow / 16), col = ch % (C::kRawRow / 16);
+                const u32x4 x = *reinterpret_cast<const u32x4*>(raw + t * C::kRawTile + ch * 16);
+                store16(cv + t * C::kTile + row * C::kPitch + col * 16, bf16x8_to_f16_bits(x));
             }
-            qst[i] = xq;
-            dst[i] = xd;
         }
         if (stid < 2 * BQ) {
-            const int query = qs0 + (stid % BQ);
-            const size_t off = ((size_t)b * Hq + h) * T + query;
-            if (stid < BQ) lst = query < T ? a.lse[off] * kLog2e : INFINITY;   // P = 0 past T
-            else lst = query < T ? a.delta[off] : 0.0f;
+            const float x = reinterpret_cast<const float*>(raw + 2 * C::kRawTile)[stid];
+            const bool valid = qs0 + (stid % BQ) < T;
+            float y;
+            if (stid < BQ) y = valid ? x * kLog2e : INFINITY;    // P = 0 past T
+            else y = valid ? x : 0.0f;
+            reinterpret_cast<float*>(cv + 2 * C::kTile)[stid] = y;
         }
     };
-    auto store_step = [&](int buf) {
-        char* qs = slot_base + buf * C::kStage;
-        char* ds = qs + C::kTile;
-        float* ls = reinterpret_cast<float*>(ds + C::kTile);
-#pragma unroll
-        for (int i = 0; i < C::kPerThread; ++i) {
-            const int ch = stid + i * C::kSlotThreads;
-            const int row = ch / (D / 8), col = ch % (D / 8);
-            store16(qs + row * C::kPitch + col * 16, bf16x8_to_f16_bits(qst[i]));
-            store16(ds + row * C::kPitch + col * 16, bf16x8_to_f16_bits(dst[i]));
-        }
-        if (stid < 2 * BQ) ls[stid] = lst;
+    auto wait_barrier = [&](int pending_steps) {
+        // pending_steps: how many of this wave's issued steps may still be in flight.
+        if (pending_steps <= 0) wait_tiles_barrier<0>();
+        else if (pending_steps == 1) wait_tiles_barrier<C::kVmPerStep>();
+        else wait_tiles_barrier<2 * C::kVmPerStep>();
     };
 
-    if (nsteps > 0) {
-        load_step(0);
-        store_step(0);
-    }
-    __syncthreads();
+    // Prologue: DMA the first NR steps, convert step 0.
+    for (int st = 0; st < NR && st < nsteps; ++st) issue_step(st);
+    wait_barrier(min(NR, nsteps) - 1);
+    if (nsteps > 0) convert_step(0);
 
     const int tr_row = (lane & 15) >> 2;
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
     for (int step = 0; step < nsteps; ++step) {
-        if (step + 1 < nsteps) load_step(step + 1);
-        const char* qs = slot_base + (step & 1) * C::kStage;
+        // Step+1 complete in LDS (only newer steps may be in flight); the barrier also
+        // retires every wave's use of the stages that the next DMA and conversion reuse.
+        wait_barrier(min(step + NR - 1, nsteps - 1) - (step + 1));
+        if (step + NR < nsteps) issue_step(step + NR);
+        if (step + 1 < nsteps) convert_step(step + 1);
+
+        const char* qs = conv_stage(step);
         const char* ds = qs + C::kTile;
         const float* lse2s = reinterpret_cast<const float*>(ds + C::kTile);
         const float* dels = lse2s + BQ;
-        const int qs0 = (qt_begin + step % per_head) * BQ;
+        const int qs0 = step_q0(step);
 
 #pragma unroll
         for (int sb = 0; sb < C::kQSB; ++sb) {
@@ -452,9 +494,8 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
                 }
             }
         }
-        if (step + 1 < nsteps) store_step((step + 1) & 1);
-        __syncthreads();
     }
+    __syncthreads();
 
     // ---- sum the head slots (ascending) and store: one 32-dim block of dK, then of dV,
     // at a time through the same LDS area; every wave's lane values line up across
@@ -516,15 +557,15 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, int BQ, int NKW, int HS>
+template <int D, int BQ, int NKW, int HS, int NR>
 static hipError_t launch_dkv_t(const BwdArgs& a, hipStream_t stream) {
-    using C = DkvCfg<D, BQ, NKW, HS>;
+    using C = DkvCfg<D, BQ, NKW, HS, NR>;
     BwdArgs x = a;
     x.n_tiles = ((a.T + 31) / 32 + NKW - 1) / NKW;
     const long blocks = (long)x.n_tiles * a.B * a.Hkv;
     // One workgroup per CU fits (LDS and registers); gfx950 parts have 256 CUs.
     x.zigzag = blocks <= 256 ? 1 : 0;
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
                        stream, x);
     return hipGetLastError();
 }
@@ -541,12 +582,12 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
 hipError_t launch_bwd_dkv(const BwdArgs& a, hipStream_t stream) {
     const int G = a.Hq / a.Hkv;
     if (a.d == 64) {
-        if (G % 4 == 0) return launch_dkv_t<64, 64, 2, 4>(a, stream);
-        if (G % 3 == 0) return launch_dkv_t<64, 32, 4, 3>(a, stream);
-        if (G % 2 == 0) return launch_dkv_t<64, 64, 4, 2>(a, stream);
-        return launch_dkv_t<64, 64, 4, 1>(a, stream);
+        if (G % 4 == 0) return launch_dkv_t<64, 32, 2, 4, 2>(a, stream);
+        if (G % 3 == 0) return launch_dkv_t<64, 32, 4, 3, 3>(a, stream);
+        if (G % 2 == 0) return launch_dkv_t<64, 32, 4, 2, 3>(a, stream);
+        return launch_dkv_t<64, 32, 4, 1, 3>(a, stream);
     }
-    return launch_dkv_t<128, 32, 4, 1>(a, stream);
+    return launch_dkv_t<128, 32, 4, 1, 3>(a, stream);
 }
 
 }  // namespace cgqa

@@ -143,6 +143,18 @@ __device__ __forceinline__ void load_lds16(const uint16_t* src, const void* lds_
         : "memory");
 }
 
+// The 4-byte variant (global_load_lds_dword): lane i's 4 bytes land at lds_base + 4 * i.
+__device__ __forceinline__ void load_lds4(const void* src, const void* lds_base) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(m0)
+        : "memory");
+}
+
 // Wait until at most N vector memory operations of this wave are outstanding and all
 // its LDS operations are done, then join the workgroup barrier. Unlike
 // __syncthreads() it leaves the newer (prefetch) loads in flight. The asm is also a
