@@ -34,6 +34,8 @@
 #include "cgqa_device.hpp"
 #include "cgqa_launch.hpp"
 
+#include <type_traits>
+
 namespace cgqa {
 
 // Physical 16-byte slot of logical chunk c in LDS row r is c ^ chunk_swizzle<D>(r).
@@ -72,6 +74,15 @@ struct FwdCfg {
     static_assert(kTile % (1024 * NW) == 0, "tile load must split evenly over the waves");
     static_assert(kLds <= 160 * 1024, "LDS budget");
 };
+
+// Calls f(integral_constant<int, 0>) .. f(integral_constant<int, N-1>) in order.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
 
 // Probabilities above this trigger a move of the reference max.
 constexpr float kRescaleLimit = 1099511627776.0f;   // 2^40
@@ -116,8 +127,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         ld_row[i] = C::kRowsPerLoad * (wave * C::kLoadsPerTensor + i) + lane / (C::kRow / 16);
         ld_chunk[i] = ld_slot ^ chunk_swizzle<D>(ld_row[i]);
     }
-    auto issue_tile = [&](int jt) {
-        char* ks = smem + (jt % C::kStages) * C::kStage;
+    auto issue_tile = [&](int stage, int jt) {
+        char* ks = smem + stage * C::kStage;
         char* vs = ks + C::kTile;
 #pragma unroll
         for (int i = 0; i < C::kLoadsPerTensor; ++i) {
@@ -129,8 +140,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         }
     };
 
-    issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
+    issue_tile(0, 0);
+    if (ntiles > 1) issue_tile(1, 1);
 
     // Q as the B operand: lane (query n, group hl) holds dims 16*kd + 8*hl .. +7.
     bf16x8 qreg[NQB][C::kKD];
@@ -167,26 +178,41 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     // second half) of a 16-row group, 8 bytes at logical column
     // 32mb + 16*((lane>>4)&1) + 4*(j%4). Rows only enter the swizzle through r % 16,
     // which does not depend on the block, so these are per-lane constants.
-    const int k_row_off = n * C::kRow;
-    const int k_swz = chunk_swizzle<D>(n);
-    const int v_r0 = 4 * hl + ((lane & 15) >> 2);
-    const int v_swz0 = chunk_swizzle<D>(v_r0), v_swz1 = chunk_swizzle<D>(v_r0 + 8);
-    const int v_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);   // + 4*mb
-    const int v_byte = 8 * (lane & 1);
+    // With the tile loop unrolled by the stage count below, every read is one of these
+    // per-lane addresses plus an immediate offset.
+    const char* kaddr[C::kKD];
+    const char* vaddr[C::kMB][2];
+    {
+        const int k_swz = chunk_swizzle<D>(n);
+#pragma unroll
+        for (int kd = 0; kd < C::kKD; ++kd) kaddr[kd] = smem + n * C::kRow + (((2 * kd + hl) ^ k_swz) << 4);
+        const int v_r0 = 4 * hl + ((lane & 15) >> 2);
+        const int v_swz[2] = {chunk_swizzle<D>(v_r0), chunk_swizzle<D>(v_r0 + 8)};
+        const int v_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+        const int v_byte = 8 * (lane & 1);
+#pragma unroll
+        for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                vaddr[mb][r] = smem + C::kTile + (v_r0 + 8 * r) * C::kRow + v_byte + (((4 * mb + v_chunk) ^ v_swz[r]) << 4);
+    }
 
-    for (int jt = 0; jt < ntiles; ++jt) {
+    for (int jt0 = 0; jt0 < ntiles; jt0 += C::kStages) {
+      static_for<C::kStages>([&](auto Uc) {
+        constexpr int U = decltype(Uc)::value;
+        constexpr int soff = U * C::kStage;
+        const int jt = jt0 + U;
+        if (jt >= ntiles) return;
         // Tile jt is complete once at most the next tile's loads are outstanding; the
         // barrier also tells every wave that all waves are done with tile jt - 1,
         // whose stage the loads of tile jt + 2 reuse.
         if (jt + 1 < ntiles) wait_tiles_barrier<C::kLoadsPerTile>();
         else wait_tiles_barrier<0>();
-        if (jt + 2 < ntiles) issue_tile(jt + 2);
+        if (jt + 2 < ntiles) issue_tile((U + 2) % C::kStages, jt + 2);
 
         const int j0 = jt * C::kBN;
-        const char* ks = smem + (jt % C::kStages) * C::kStage;
-        const char* vs = ks + C::kTile;
 
-        if (qw + 32 * NQB - 1 < j0) continue;   // every query of this wave is before the tile
+        if (qw + 32 * NQB - 1 < j0) return;   // every query of this wave is before the tile
 #pragma unroll
         for (int kb = 0; kb < C::kNKB; ++kb) {
             const int jb = j0 + 32 * kb;
@@ -195,13 +221,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
             // diagonal. Register i of block qb is key jb + 8(i/4) + 4hl + i%4.
             f32x16 s[NQB];
             const bool need_mask = (jb + 31 > qw);
-            const char* krow = ks + 32 * kb * C::kRow + k_row_off;
+            const int koff = soff + 32 * kb * C::kRow;
             auto scores = [&]() {
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) s[qb] = zero16();
 #pragma unroll
                 for (int kd = 0; kd < C::kKD; ++kd) {
-                    const bf16x8 ka = lds_read8(krow + (((2 * kd + hl) ^ k_swz) << 4));
+                    const bf16x8 ka = lds_read8(kaddr[kd] + koff);
 #pragma unroll
                     for (int qb = 0; qb < NQB; ++qb) s[qb] = mfma32x32x16(ka, qreg[qb][kd], s[qb]);
                 }
@@ -277,18 +303,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
                 bf16x8 pb[NQB];
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) pb[qb] = t == 0 ? pack_lo(s[qb]) : pack_hi(s[qb]);
-                const char* vrow0 = vs + (32 * kb + 16 * t + v_r0) * C::kRow + v_byte;
-                const char* vrow1 = vrow0 + 8 * C::kRow;
+                const int voff = soff + (32 * kb + 16 * t) * C::kRow;
 #pragma unroll
                 for (int mb = 0; mb < C::kMB; ++mb) {
-                    const int ch = 4 * mb + v_chunk;
-                    const bf16x8 va = concat(lds_read_tr4(vrow0 + ((ch ^ v_swz0) << 4)),
-                                             lds_read_tr4(vrow1 + ((ch ^ v_swz1) << 4)));
+                    const bf16x8 va = concat(lds_read_tr4(vaddr[mb][0] + voff), lds_read_tr4(vaddr[mb][1] + voff));
 #pragma unroll
                     for (int qb = 0; qb < NQB; ++qb) oacc[qb][mb] = mfma32x32x16(va, pb[qb], oacc[qb][mb]);
                 }
             }
         }
+      });
     }
 
     // ---- epilogue: O = acc / l in bf16, LSE = ln2 * (m + log2 l).

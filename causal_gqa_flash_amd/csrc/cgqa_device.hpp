@@ -24,6 +24,8 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
@@ -141,6 +143,54 @@ __device__ __forceinline__ void load_lds16(const uint16_t* src, const void* lds_
         : "=&s"(saved)
         : "v"(src), "s"(m0)
         : "memory");
+}
+
+// As load_lds16, with the address split into a wave-uniform base (SGPR pair) and a
+// per-lane 32-bit byte offset: one VGPR per lane instead of a 64-bit address pair.
+__device__ __forceinline__ void load_lds16_off(const void* base, unsigned off, const void* lds_base) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
+    // readfirstlane returns int: both halves are zero-extended through uint32_t (a
+    // sign-extended low half would set every bit of the high word).
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)base);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)((uintptr_t)base >> 32));
+    const uint64_t sbase = lo | (hi << 32);
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(sbase), "s"(m0)
+        : "memory");
+}
+
+// N (1, 2 or 4) consecutive 1 KB chunks in one asm block, M0 saved and restored once.
+// Chunk e lands at LDS byte address lds + 1024 * e + 16 * lane and reads global
+// address base + off[e] + 1024 * e (the instruction offset applies to both), so
+// callers pass off[e] already reduced by 1024 * e. base and lds are wave-uniform.
+template <int N>
+__device__ __forceinline__ void load_lds16_chunks(const void* base, const unsigned (&off)[N], unsigned lds) {
+    static_assert(N == 1 || N == 2 || N == 4, "chunk count");
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)base);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)((uintptr_t)base >> 32));
+    const uint64_t sbase = lo | (hi << 32);
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds);
+    unsigned saved;
+    if constexpr (N == 1) {
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, %3\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved) : "v"(off[0]), "s"(m0), "s"(sbase) : "memory");
+    } else if constexpr (N == 2) {
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\t"
+                     "global_load_lds_dwordx4 %1, %4\n\tglobal_load_lds_dwordx4 %2, %4 offset:1024\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved) : "v"(off[0]), "v"(off[1]), "s"(m0), "s"(sbase) : "memory");
+    } else {
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %5\n\t"
+                     "global_load_lds_dwordx4 %1, %6\n\tglobal_load_lds_dwordx4 %2, %6 offset:1024\n\t"
+                     "global_load_lds_dwordx4 %3, %6 offset:2048\n\tglobal_load_lds_dwordx4 %4, %6 offset:3072\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved) : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(m0), "s"(sbase)
+                     : "memory");
+    }
 }
 
 // The 4-byte variant (global_load_lds_dword): lane i's 4 bytes land at lds_base + 4 * i.
