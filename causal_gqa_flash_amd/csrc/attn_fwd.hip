@@ -34,7 +34,10 @@
 #include "cgqa_device.hpp"
 #include "cgqa_launch.hpp"
 
+#include <string.h>
+
 #include <type_traits>
+#include <vector>
 
 namespace cgqa {
 
@@ -94,9 +97,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
 
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
     const int bh_count = a.B * Hq;
-    const int bid = blockIdx.x;
-    const int qt = a.n_qtiles - 1 - bid / bh_count;   // heaviest query block first
-    const int bh = bid % bh_count;
+    // Task t: query tile n_qtiles-1 - t / bh_count of (batch, head) t % bh_count, so the
+    // default order starts the heaviest tiles first; small grids use the host's map.
+    const int task = a.use_map ? (int)a.task_map[blockIdx.x] : (int)blockIdx.x;
+    const int qt = a.n_qtiles - 1 - task / bh_count;
+    const int bh = task % bh_count;
     const int b = bh / Hq, h = bh % Hq;
     const int g = h / (Hq / Hkv);
 
@@ -338,12 +343,56 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     }
 }
 
+// Balanced placement for grids of at most three workgroups per CU. All of them are
+// resident at once, and the dispatcher places workgroup x on CU x mod n_cu (measured on
+// MI355X: x, x + 256 and x + 512 share a CU). A task's load is proportional to its
+// number of key tiles, n_qtiles - t / bh_count; the longest tasks are dealt first,
+// each to the least loaded CU with a free slot. A different placement only costs
+// balance, never correctness.
+static bool build_task_map(int blocks, int bh_count, int n_qtiles, int n_cu, uint16_t* map) {
+    if (n_cu <= 0 || blocks > kFwdMaxMapped || blocks > 3 * n_cu || blocks <= n_cu) return false;
+    struct Cache { int blocks = -1, bh = -1, nq = -1, ncu = -1; uint16_t map[kFwdMaxMapped]; };
+    thread_local Cache cache;
+    if (cache.blocks == blocks && cache.bh == bh_count && cache.nq == n_qtiles && cache.ncu == n_cu) {
+        memcpy(map, cache.map, sizeof(uint16_t) * blocks);
+        return true;
+    }
+    std::vector<int> load(n_cu, 0), used(n_cu, 0);
+    // Tasks are already in decreasing load order (t increases as the tile gets lighter).
+    for (int t = 0; t < blocks; ++t) {
+        const int w = n_qtiles - t / bh_count;
+        int best = -1;
+        for (int c = 0; c < n_cu; ++c) {
+            if (c + used[c] * n_cu >= blocks) continue;   // no free slot on this CU
+            if (best < 0 || load[c] < load[best]) best = c;
+        }
+        map[best + used[best] * n_cu] = (uint16_t)t;
+        ++used[best];
+        load[best] += w;
+    }
+    cache.blocks = blocks;
+    cache.bh = bh_count;
+    cache.nq = n_qtiles;
+    cache.ncu = n_cu;
+    memcpy(cache.map, map, sizeof(uint16_t) * blocks);
+    return true;
+}
+
+static int device_cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
+
 template <int D, int NQB, int BN, int NW>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     using C = FwdCfg<D, NQB, BN, NW>;
     FwdArgs x = a;
     x.n_qtiles = (a.T + C::kBM - 1) / C::kBM;
     const long blocks = (long)x.n_qtiles * a.B * a.Hq;
+    x.use_map = blocks <= kFwdMaxMapped &&
+                build_task_map((int)blocks, a.B * a.Hq, x.n_qtiles, device_cu_count(), x.task_map);
     hipLaunchKernelGGL((attn_fwd_kernel<D, NQB, BN, NW>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, x);
     return hipGetLastError();
 }

@@ -6,6 +6,10 @@
 
 namespace cgqa {
 
+// Largest grid the forward launcher balances with an explicit task map: three rounds
+// of workgroups on 256 CUs (all resident at once).
+constexpr int kFwdMaxMapped = 768;
+
 struct FwdArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -15,6 +19,8 @@ struct FwdArgs {
     int B, T, Hq, Hkv, d;
     float scale_log2;   // scale * log2(e): scores in log2 units
     int n_qtiles;       // set by the launcher
+    int use_map;        // set by the launcher: task of workgroup x is task_map[x]
+    uint16_t task_map[kFwdMaxMapped];
 };
 
 struct BwdArgs {
