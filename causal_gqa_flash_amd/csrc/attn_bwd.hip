@@ -45,7 +45,7 @@ struct DqCfg {
     static constexpr int kKD = D / 16;
     static constexpr int kNKB = BN / 32;
     static constexpr int kMB = D / 32;
-    static constexpr int kPitch = D * 2 + 16;     // K and V rows in LDS (fp16)
+    static constexpr int kPitch = D * 2 + 16;     // K (fp16) and V (bf16) rows in LDS
     static constexpr int kTile = BN * kPitch;
     static constexpr int kStage = 2 * kTile;
     static constexpr int kLds = 2 * kStage;
@@ -81,8 +81,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     const uint16_t* kbase = a.k + ((size_t)b * T * Hkv + g) * D;
     const uint16_t* vbase = a.v + ((size_t)b * T * Hkv + g) * D;
 
-    // Q and dO as B operands (lane: query n, dims 16*kd + 8*hl .. +7), D~ and LSE.
-    f16x8 qreg[NQB][C::kKD], doreg[NQB][C::kKD];
+    // Q (fp16) and dO (bf16, as given) as B operands (lane: query n, dims 16*kd + 8*hl
+    // .. +7), D~ and LSE. dP = V dO^T multiplies inputs only, so it runs in bf16
+    // exactly as in fp16; the products with computed P and dS~ use K in fp16.
+    f16x8 qreg[NQB][C::kKD];
+    bf16x8 doreg[NQB][C::kKD];
     float dtilde[NQB], lse2[NQB], dexact[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
                 xo = load16(a.o + off);
             }
             qreg[qb][kd] = bf16x8_to_f16(xq);
-            doreg[qb][kd] = bf16x8_to_f16(xd);
+            doreg[qb][kd] = __builtin_bit_cast(bf16x8, xd);
             const bf16x8 dv8 = __builtin_bit_cast(bf16x8, xd);
             const bf16x8 ov8 = __builtin_bit_cast(bf16x8, xo);
 #pragma unroll
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
             const int c = tid + i * C::kThreads;
             const int row = c / (D / 8), col = c % (D / 8);
             store16(ks + row * C::kPitch + col * 16, bf16x8_to_f16_bits(kst[i]));
-            store16(vs + row * C::kPitch + col * 16, bf16x8_to_f16_bits(vst[i]));
+            store16(vs + row * C::kPitch + col * 16, vst[i]);
         }
     };
 
@@ -154,78 +157,91 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     const int tr_row = (lane & 15) >> 2;
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    for (int jt = 0; jt < ntiles; ++jt) {
-        const int j0 = jt * BN;
-        if (jt + 1 < ntiles) load_tile(j0 + BN);
-        const char* ks = smem + (jt & 1) * C::kStage;
+    // One key tile against this wave's queries, from LDS buffer U. Only tiles that
+    // reach past the wave's first query need the causal mask (MASK).
+    auto tile = [&](auto Uc, auto Mc, int j0) {
+        constexpr int U = decltype(Uc)::value;
+        constexpr bool MASK = decltype(Mc)::value;
+        const char* ks = smem + U * C::kStage;
         const char* vs = ks + C::kTile;
-
-        if (qw + 32 * NQB - 1 >= j0) {
-            f32x16 s[C::kNKB][NQB], dp[C::kNKB][NQB];
+        f32x16 s[C::kNKB][NQB], dp[C::kNKB][NQB];
+#pragma unroll
+        for (int kb = 0; kb < C::kNKB; ++kb) {
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) { s[kb][qb] = zero16(); dp[kb][qb] = zero16(); }
+#pragma unroll
+            for (int kd = 0; kd < C::kKD; ++kd) {
+                const int off = (32 * kb + n) * C::kPitch + (16 * kd + 8 * hl) * 2;
+                const f16x8 ka = lds_read8_f16(ks + off);
+                const bf16x8 va = lds_read8(vs + off);
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) {
+                    s[kb][qb] = mfma32x32x16(ka, qreg[qb][kd], s[kb][qb]);
+                    dp[kb][qb] = mfma32x32x16(va, doreg[qb][kd], dp[kb][qb]);
+                }
+            }
+        }
+        // P^T into s, dS~^T into dp; the exact D on the side.
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            const int rel = j0 + 4 * hl - (qw + 32 * qb + n);   // key - query at kb = i = 0
 #pragma unroll
             for (int kb = 0; kb < C::kNKB; ++kb) {
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) { s[kb][qb] = zero16(); dp[kb][qb] = zero16(); }
-#pragma unroll
-                for (int kd = 0; kd < C::kKD; ++kd) {
-                    const int off = (32 * kb + n) * C::kPitch + (16 * kd + 8 * hl) * 2;
-                    const f16x8 ka = lds_read8_f16(ks + off);
-                    const f16x8 va = lds_read8_f16(vs + off);
-#pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) {
-                        s[kb][qb] = mfma32x32x16(ka, qreg[qb][kd], s[kb][qb]);
-                        dp[kb][qb] = mfma32x32x16(va, doreg[qb][kd], dp[kb][qb]);
+                for (int i = 0; i < 16; ++i) {
+                    float p = exp2_fast(fmaf(s[kb][qb][i], a.scale_log2, -lse2[qb]));
+                    if constexpr (MASK) {
+                        if (rel + 32 * kb + 8 * (i >> 2) + (i & 3) > 0) p = 0.0f;
                     }
+                    dexact[qb] = fmaf(p, dp[kb][qb][i], dexact[qb]);
+                    dp[kb][qb][i] = p * (dp[kb][qb][i] - dtilde[qb]);
+                    s[kb][qb][i] = p;
                 }
             }
-            // P^T into s, dS~^T into dp; the exact D on the side.
-            const bool need_mask = (j0 + BN - 1 > qw);
+        }
+        // dQ~^T += K^T dS~^T and K_bar^T += K^T P^T (B from registers, A = K^T read
+        // transposed from the K tile).
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-                const int query = qw + 32 * qb + n;
+        for (int kb = 0; kb < C::kNKB; ++kb) {
 #pragma unroll
-                for (int kb = 0; kb < C::kNKB; ++kb) {
+            for (int t = 0; t < 2; ++t) {
+                f16x8 db[NQB], pb[NQB];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        float p = exp2_fast(fmaf(s[kb][qb][i], a.scale_log2, -lse2[qb]));
-                        if (need_mask) {
-                            const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * hl + (i & 3);
-                            if (key > query) p = 0.0f;
-                        }
-                        dexact[qb] = fmaf(p, dp[kb][qb][i], dexact[qb]);
-                        dp[kb][qb][i] = p * (dp[kb][qb][i] - dtilde[qb]);
-                        s[kb][qb][i] = p;
-                    }
+                for (int qb = 0; qb < NQB; ++qb) {
+                    db[qb] = t == 0 ? pack_lo_f16(dp[kb][qb]) : pack_hi_f16(dp[kb][qb]);
+                    pb[qb] = t == 0 ? pack_lo_f16(s[kb][qb]) : pack_hi_f16(s[kb][qb]);
                 }
-            }
-            // dQ~^T += K^T dS~^T and K_bar^T += K^T P^T (B from registers, A = K^T read
-            // transposed from the K tile).
+                const int r0 = 32 * kb + 16 * t + 4 * hl + tr_row;
 #pragma unroll
-            for (int kb = 0; kb < C::kNKB; ++kb) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    f16x8 db[NQB], pb[NQB];
+                for (int mb = 0; mb < C::kMB; ++mb) {
+                    const char* p0 = ks + r0 * C::kPitch + (32 * mb + tr_col) * 2;
+                    const f16x8 kt = concat(lds_read_tr4_f16(p0), lds_read_tr4_f16(p0 + 8 * C::kPitch));
 #pragma unroll
                     for (int qb = 0; qb < NQB; ++qb) {
-                        db[qb] = t == 0 ? pack_lo_f16(dp[kb][qb]) : pack_hi_f16(dp[kb][qb]);
-                        pb[qb] = t == 0 ? pack_lo_f16(s[kb][qb]) : pack_hi_f16(s[kb][qb]);
-                    }
-                    const int r0 = 32 * kb + 16 * t + 4 * hl + tr_row;
-#pragma unroll
-                    for (int mb = 0; mb < C::kMB; ++mb) {
-                        const char* p0 = ks + r0 * C::kPitch + (32 * mb + tr_col) * 2;
-                        const f16x8 kt = concat(lds_read_tr4_f16(p0), lds_read_tr4_f16(p0 + 8 * C::kPitch));
-#pragma unroll
-                        for (int qb = 0; qb < NQB; ++qb) {
-                            dqacc[qb][mb] = mfma32x32x16(kt, db[qb], dqacc[qb][mb]);
-                            kbar[qb][mb] = mfma32x32x16(kt, pb[qb], kbar[qb][mb]);
-                        }
+                        dqacc[qb][mb] = mfma32x32x16(kt, db[qb], dqacc[qb][mb]);
+                        kbar[qb][mb] = mfma32x32x16(kt, pb[qb], kbar[qb][mb]);
                     }
                 }
             }
         }
-        if (jt + 1 < ntiles) store_tile((jt + 1) & 1);
-        __syncthreads();
+    };
+
+    // Two LDS buffers; the loop is unrolled by two so each buffer's offsets are
+    // immediates. The next tile's global loads run during the current tile.
+    for (int jt0 = 0; jt0 < ntiles; jt0 += 2) {
+        static_for<2>([&](auto Uc) {
+            constexpr int U = decltype(Uc)::value;
+            const int jt = jt0 + U;
+            if (jt >= ntiles) return;
+            const int j0 = jt * BN;
+            if (jt + 1 < ntiles) load_tile(j0 + BN);
+            if (qw + 32 * NQB - 1 >= j0) {
+                if (j0 + BN - 1 > qw) tile(Uc, std::true_type{}, j0);
+                else tile(Uc, std::false_type{}, j0);
+            }
+            if (jt + 1 < ntiles) store_tile(1 - U);
+            __syncthreads();
+        });
     }
 
 #pragma unroll
@@ -571,7 +587,7 @@ static hipError_t launch_dkv_t(const BwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
-    if (a.d == 64) return launch_dq_t<64, 1, 64, 4>(a, stream);
+    if (a.d == 64) return launch_dq_t<64, 1, 32, 4>(a, stream);
     return launch_dq_t<128, 1, 32, 4>(a, stream);
 }
 

@@ -78,15 +78,6 @@ struct FwdCfg {
     static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
-// Calls f(integral_constant<int, 0>) .. f(integral_constant<int, N-1>) in order.
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (N > 0) {
-        static_for<N - 1>(f);
-        f(std::integral_constant<int, N - 1>{});
-    }
-}
-
 // Probabilities above this trigger a move of the reference max.
 constexpr float kRescaleLimit = 1099511627776.0f;   // 2^40
 

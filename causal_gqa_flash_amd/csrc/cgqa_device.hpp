@@ -13,6 +13,8 @@
 // matrix stored [k][n] becomes an MFMA operand whose slots run along k.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 namespace cgqa {
@@ -203,6 +205,16 @@ __device__ __forceinline__ void load_lds4(const void* src, const void* lds_base)
         : "=&s"(saved)
         : "v"(src), "s"(m0)
         : "memory");
+}
+
+// Calls f(integral_constant<int, 0>) .. f(integral_constant<int, N-1>) in order: an
+// unrolled loop whose index is a compile-time constant in the body.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
 }
 
 // Wait until at most N vector memory operations of this wave are outstanding and all
