@@ -562,6 +562,275 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     reduce_store(dvacc, a.dv, 1.0f);
 }
 
+// ---- Software-pipelined dQ (d = 64) ---------------------------------------------------
+//
+// Workgroup: 4 waves x 32 queries of one head; a step is one 32-key block. In step t a
+// wave issues dQ~ += K^T dS~(t-1) and K_bar += K^T P(t-1) on the fp16 matrix core while
+// its vector ALU turns block t into P, dS~ and the exact D, then issues S^T(t+1) = K Q^T
+// and dP^T(t+1) = V dO^T on the bf16 matrix core (inputs straight from the raw tiles:
+// bf16 products are exact in fp32) into the registers block t just released. Raw K and V arrive by direct-to-LDS loads in a 4-stage ring
+// (3 steps ahead); K is also converted once to fp16 into a 4-slot padded ring for the
+// transposing reads. K(u) is read raw in step u-1 (scores, conversion) and in fp16 in
+// step u+1; V(u) in step u-1.
+template <int D>
+struct DqPipeCfg {
+    static constexpr int kNW = 4;
+    static constexpr int kThreads = 64 * kNW;
+    static constexpr int kBM = 32 * kNW;             // queries per workgroup
+    static constexpr int kKD = D / 16;
+    static constexpr int kMB = D / 32;
+    static constexpr int kRow = 2 * D;               // raw bf16 row (swizzled chunks)
+    static constexpr int kTile = 32 * kRow;          // raw K (or V) of a 32-key block
+    static constexpr int kRawStage = 2 * kTile;      // K then V
+    static constexpr int kDepth = 4;
+    static constexpr int kRaw = kDepth * kRawStage;
+    static constexpr int kPitch = 2 * D + 16;        // fp16 K rows, padded
+    static constexpr int kHalfTile = 32 * kPitch;
+    static constexpr int kLds = kRaw + kDepth * kHalfTile;
+    static constexpr int kChunks = kTile / 1024;     // 1 KB DMA chunks per tensor
+    static constexpr int kRowsPerChunk = 1024 / kRow;
+    static_assert(kChunks == kNW, "one K and one V chunk per wave and step");
+    static_assert(kLds <= 160 * 1024, "LDS budget");
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
+    using C = DqPipeCfg<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
+    char* const raw = smem;
+    char* const k16 = smem + C::kRaw;
+
+    // Workgroup-uniform indices (readfirstlane keeps the integer divisions' results,
+    // and everything derived from them, in scalar registers).
+    const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
+    const int bh_count = a.B * Hq;
+    const int bid = blockIdx.x;
+    const int qt = __builtin_amdgcn_readfirstlane(a.n_tiles - 1 - bid / bh_count);   // heaviest first
+    const int bh = __builtin_amdgcn_readfirstlane(bid % bh_count);
+    const int b = __builtin_amdgcn_readfirstlane(bh / Hq);
+    const int h = __builtin_amdgcn_readfirstlane(bh % Hq);
+    const int g = __builtin_amdgcn_readfirstlane(h / (Hq / Hkv));
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, hl = lane >> 5;
+    const int q0 = qt * C::kBM;
+    const int qw = q0 + 32 * wave;                    // first query of this wave
+    const int nb_wg = (min(T, q0 + C::kBM) + 31) / 32; // key blocks the workgroup needs
+    const int my_n = (qw < T) ? qw / 32 + 1 : 0;      // key blocks of this wave
+
+    const size_t q_stride = (size_t)Hq * D;
+    const size_t kv_stride = (size_t)Hkv * D;
+    const size_t qoff = ((size_t)b * T * Hq + h) * D;
+    const uint16_t* kbase = a.k + ((size_t)b * T * Hkv + g) * D;
+    const uint16_t* vbase = a.v + ((size_t)b * T * Hkv + g) * D;
+    const unsigned kv_row_bytes = (unsigned)kv_stride * 2u;
+
+    // DMA: wave w loads chunk w (rows 8w .. 8w+7 for D = 64) of K and of V of a block.
+    // Blocks outside 0 .. nb_wg-1 reload the last block (into a stage nobody reads), so
+    // every step issues the same two full-wave loads and the waits are constants. In the
+    // last block of a ragged sequence, rows past T repeat row T-1 (finite data; those
+    // keys are masked for every real query).
+    const int ld_r = C::kRowsPerChunk * wave + lane / (C::kRow / 16);
+    const unsigned voff = (unsigned)ld_r * kv_row_bytes +
+                          (unsigned)((lane % (C::kRow / 16)) ^ chunk_swizzle<D>(ld_r)) * 16u;
+    const unsigned lds0 = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)smem);
+    auto issue = [&](int stage, int u) {
+        const int uc = min(max(u, 0), nb_wg - 1);
+        const int rows = T - 32 * uc;
+        const unsigned lds = lds0 + stage * C::kRawStage + wave * 1024;
+        const char* kb = reinterpret_cast<const char*>(kbase) + (size_t)(32 * uc) * kv_row_bytes;
+        const char* vb = reinterpret_cast<const char*>(vbase) + (size_t)(32 * uc) * kv_row_bytes;
+        const unsigned o[1] = {rows >= 32 ? voff
+                                          : (unsigned)min(ld_r, rows - 1) * kv_row_bytes +
+                                                (unsigned)((lane % (C::kRow / 16)) ^ chunk_swizzle<D>(ld_r)) * 16u};
+        load_lds16_chunks<1>(kb, o, lds);
+        load_lds16_chunks<1>(vb, o, lds + C::kTile);
+    };
+#pragma unroll
+    for (int u = 0; u < 3; ++u) issue(u, u);   // what steps -4 .. -2 issue
+
+    // Q, dO (bf16, as given) as B operands (lane: query n, dims 16*kd + 8*hl .. +7),
+    // D~ = rowsum(dO * O) from the given bf16 O, and the row's LSE in log2 units.
+    bf16x8 qreg[C::kKD], doreg[C::kKD];
+    float dtilde, lse2, dexact = 0.0f;
+    {
+        const int row = qw + n;
+        float part = 0.0f;
+#pragma unroll
+        for (int kd = 0; kd < C::kKD; ++kd) {
+            u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u}, xo = {0u, 0u, 0u, 0u};
+            if (row < T) {
+                const size_t off = qoff + (size_t)row * q_stride + 16 * kd + 8 * hl;
+                xq = load16(a.q + off);
+                xd = load16(a.dO + off);
+                xo = load16(a.o + off);
+            }
+            qreg[kd] = __builtin_bit_cast(bf16x8, xq);
+            doreg[kd] = __builtin_bit_cast(bf16x8, xd);
+            const bf16x8 dv8 = __builtin_bit_cast(bf16x8, xd);
+            const bf16x8 ov8 = __builtin_bit_cast(bf16x8, xo);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part += (float)dv8[e] * (float)ov8[e];
+        }
+        part += swap_halves(part);
+        dtilde = part;
+        lse2 = row < T ? a.lse[((size_t)b * Hq + h) * T + row] * kLog2e : 0.0f;
+#pragma unroll
+        for (int kd = 0; kd < C::kKD; ++kd) asm volatile("" ::"v"(qreg[kd]), "v"(doreg[kd]));
+    }
+
+    f32x16 dqacc[C::kMB], kbar[C::kMB];
+#pragma unroll
+    for (int mb = 0; mb < C::kMB; ++mb) { dqacc[mb] = zero16(); kbar[mb] = zero16(); }
+    // S^T and dP^T of the block being turned into probabilities, and the fp16 P and
+    // dS~ (two B operands each) of the previous block: the products of block t-1 are
+    // issued (and read their operands) before block t's softmax overwrites them.
+    f32x16 sc = zero16(), dpc = zero16();
+    f16x8 pk[2] = {f16x8{}, f16x8{}}, dsk[2] = {f16x8{}, f16x8{}};
+
+    // Per-lane LDS addresses. A operand rows (raw tile): row n, logical chunk 2kd + hl.
+    // Transposing reads of fp16 K: rows 16tt + 4hl + (lane&15)/4 (+8), columns
+    // 32mb + 16((lane>>4)&1) + 4(lane&3).
+    const char* aaddr[C::kKD];
+    {
+        const int swz = chunk_swizzle<D>(n);
+#pragma unroll
+        for (int kd = 0; kd < C::kKD; ++kd) aaddr[kd] = raw + n * C::kRow + (((2 * kd + hl) ^ swz) << 4);
+    }
+    const char* traddr = k16 + (4 * hl + ((lane & 15) >> 2)) * C::kPitch +
+                         2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    // Conversion of a raw K block to fp16: thread tid takes row tid/8, logical chunk tid%8.
+    const int cv_r = tid / (C::kRow / 16), cv_c = tid % (C::kRow / 16);
+    const char* cv_src = raw + cv_r * C::kRow + ((cv_c ^ chunk_swizzle<D>(cv_r)) << 4);
+    char* cv_dst = k16 + cv_r * C::kPitch + cv_c * 16;
+
+    // (ALWAYS: the caller knows block t+1 exists.)
+    auto sync_and_stage = [&](int t, int iss, int rst, int cst, auto Ac) {
+        // Loads of steps t-2 and t-1 (two per wave and step) may stay in flight; the
+        // older ones hold K(t+1) and V(t+1).
+        wait_tiles_barrier<4>();
+        issue(iss, t + 4);                    // into the stage K(t), V(t) left
+        if (decltype(Ac)::value || t + 1 < nb_wg) {
+            const u32x4 x = __builtin_bit_cast(u32x4, lds_read8(cv_src + rst * C::kRawStage));
+            store16(cv_dst + cst * C::kHalfTile, bf16x8_to_f16_bits(x));
+        }
+    };
+    // Scores and dP of block t+1 (bf16 matrix core).
+    auto mfma_sdp = [&](int rst, f32x16& sn, f32x16& dpn) {
+        bf16x8 ka[C::kKD], va[C::kKD];
+#pragma unroll
+        for (int kd = 0; kd < C::kKD; ++kd) {
+            ka[kd] = lds_read8(aaddr[kd] + rst * C::kRawStage);
+            va[kd] = lds_read8(aaddr[kd] + rst * C::kRawStage + C::kTile);
+        }
+        sn = zero16();
+        dpn = zero16();
+#pragma unroll
+        for (int kd = 0; kd < C::kKD; ++kd) {
+            sn = mfma32x32x16(ka[kd], qreg[kd], sn);
+            dpn = mfma32x32x16(va[kd], doreg[kd], dpn);
+        }
+    };
+    // P, dS~ and D of block t; the mask only on the wave's diagonal block.
+    // (In place: the scores become P, dP becomes dS~; both are dead afterwards.)
+    // The steady steps never meet the diagonal and take MAY_MASK = false: a run-time
+    // test alone would be if-converted and the comparisons executed on every block.
+    auto softmax = [&](auto Mc, int t, f32x16& sc, f32x16& dpc, f16x8 (&pk)[2], f16x8 (&dk)[2]) {
+        constexpr bool MAY_MASK = decltype(Mc)::value;
+        const bool diag = t == my_n - 1;
+        const int rel = 32 * t + 4 * hl - (qw + n);   // key - query at i = 0
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float e = exp2_fast(fmaf(sc[i], a.scale_log2, -lse2));
+            if constexpr (MAY_MASK)
+                if (diag && rel + 8 * (i >> 2) + (i & 3) > 0) e = 0.0f;
+            dexact = fmaf(e, dpc[i], dexact);
+            dpc[i] = e * (dpc[i] - dtilde);
+            sc[i] = e;
+        }
+        pk[0] = pack_lo_f16(sc);
+        pk[1] = pack_hi_f16(sc);
+        dk[0] = pack_lo_f16(dpc);
+        dk[1] = pack_hi_f16(dpc);
+    };
+    // dQ~^T += K^T dS~^T and K_bar^T += K^T P^T for block t-1 (fp16 matrix core).
+    auto mfma_dq = [&](int cst, const f16x8 (&pk)[2], const f16x8 (&dk)[2]) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+            for (int mb = 0; mb < C::kMB; ++mb) {
+                const char* p0 = traddr + cst * C::kHalfTile + 16 * tt * C::kPitch + 64 * mb;
+                const f16x8 kt = concat(lds_read_tr4_f16(p0), lds_read_tr4_f16(p0 + 8 * C::kPitch));
+                dqacc[mb] = mfma32x32x16(kt, dk[tt], dqacc[mb]);
+                kbar[mb] = mfma32x32x16(kt, pk[tt], kbar[mb]);
+            }
+        }
+    };
+
+    // Edge steps with run-time stages (P: parity of t).
+    auto edge_step = [&](int t) {
+        sync_and_stage(t, (t + 4) & 3, (t + 1) & 3, (t + 1) & 3, std::false_type{});
+        if (t >= 1 && t - 1 < my_n) mfma_dq((t + 3) & 3, pk, dsk);
+        if (t >= 0 && t < my_n) softmax(std::true_type{}, t, sc, dpc, pk, dsk);
+        if (t + 1 < my_n) mfma_sdp((t + 1) & 3, sc, dpc);
+    };
+    edge_step(-1);
+    edge_step(0);
+    // Steady steps t = 1 .. my_n-2 in whole groups of four: copy U of a group handles
+    // t = 4k + 1 + U, with raw stage and conversion slot (2 + U) % 4 for block t+1,
+    // fp16 slot U % 4 for block t-1 and DMA stage (1 + U) % 4 known at compile time.
+    // No copy leaves the loop early, so the accumulators stay in the same registers
+    // across the copies; the 0-3 remaining steady steps take the run-time path.
+    const int n_groups = max(0, my_n - 2) / 4;
+    for (int k = 0; k < n_groups; ++k) {
+        static_for<4>([&](auto Uc) {
+            constexpr int U = decltype(Uc)::value;
+            const int t = 4 * k + 1 + U;
+            sync_and_stage(t, (1 + U) % 4, (2 + U) % 4, (2 + U) % 4, std::true_type{});
+            mfma_dq(U % 4, pk, dsk);
+            softmax(std::false_type{}, t, sc, dpc, pk, dsk);
+            mfma_sdp((2 + U) % 4, sc, dpc);
+        });
+    }
+    for (int t = 4 * n_groups + 1; t <= my_n - 2; ++t) edge_step(t);
+    // The wave's last two steps with work, then the workgroup's remaining steps (loads
+    // and conversions for the other waves).
+    const int t_last = max(1, my_n - 1);
+    edge_step(t_last);
+    edge_step(t_last + 1);
+    for (int t = t_last + 2; t <= nb_wg; ++t) sync_and_stage(t, (t + 4) & 3, (t + 1) & 3, (t + 1) & 3, std::false_type{});
+
+    const int query = qw + n;
+    const float dfull = dexact + swap_halves(dexact);
+    if (query < T) {
+        if (hl == 0) a.delta[((size_t)b * Hq + h) * T + query] = dfull;
+        const float corr = dfull - dtilde;
+        float* drow = a.dq + qoff + (size_t)query * q_stride;
+#pragma unroll
+        for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                f32x4 x;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[r] = a.scale * fmaf(-corr, kbar[mb][4 * u + r], dqacc[mb][4 * u + r]);
+                *reinterpret_cast<f32x4*>(drow + 32 * mb + 8 * u + 4 * hl) = x;
+            }
+    }
+}
+
+template <int D>
+static hipError_t launch_dq_pipe(const BwdArgs& a, hipStream_t stream) {
+    using C = DqPipeCfg<D>;
+    BwdArgs x = a;
+    x.n_tiles = (a.T + C::kBM - 1) / C::kBM;
+    const long blocks = (long)x.n_tiles * a.B * a.Hq;
+    hipLaunchKernelGGL((attn_bwd_dq_pipe_kernel<D>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, x);
+    return hipGetLastError();
+}
+
 template <int D, int NQB, int BN, int NW>
 static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream) {
     using C = DqCfg<D, NQB, BN, NW>;
@@ -587,7 +856,7 @@ static hipError_t launch_dkv_t(const BwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
-    if (a.d == 64) return launch_dq_t<64, 1, 32, 4>(a, stream);
+    if (a.d == 64) return launch_dq_pipe<64>(a, stream);
     return launch_dq_t<128, 1, 32, 4>(a, stream);
 }
 

@@ -41,22 +41,6 @@
 
 namespace cgqa {
 
-// Physical 16-byte slot of logical chunk c in LDS row r is c ^ chunk_swizzle<D>(r).
-// LDS serves 64 banks x 4 bytes per clock: a D=64 row (128 B) is half a bank window,
-// a D=128 row a whole one. For 16 lanes reading the same chunk of 16 consecutive rows
-// (the K operand) every (row parity, slot) pair, resp. slot, must differ; for a
-// transposing read (4 consecutive rows, an aligned pair of chunks) the slot pairs of
-// rows that share a bank window must differ. Both hold for these maps.
-template <int D>
-__device__ __forceinline__ int chunk_swizzle(int r) {
-    if constexpr (D == 64) {
-        const int u = (r >> 1) & 7;
-        return ((u & 1) << 2) | (((u >> 2) & 1) << 1) | ((u >> 1) & 1);
-    } else {
-        return ((r & 7) << 1) | ((r >> 3) & 1);
-    }
-}
-
 template <int D, int NQB, int BN, int NW>
 struct FwdCfg {
     static constexpr int kThreads = NW * 64;
