@@ -16,114 +16,189 @@
 //    O^T += V^T P^T: no trip through LDS for P (the role the pages give to their
 //    C-fragment to A-fragment match). V^T comes from the row-major V tile through the
 //    transposing LDS read.
-//  * The reference max is not updated tile by tile. Softmax is invariant to the
+//  * Software pipeline inside each wave. On gfx950 the vector ALU and the matrix core
+//    only overlap well when one wave interleaves independent work for both; work of
+//    two different waves on one SIMD mostly adds up. So the wave's step j issues the
+//    scores of key block j+1 and the P.V product of block j-1 on the matrix core,
+//    interleaved with the softmax of block j on the vector ALU (which depends on
+//    neither). The diagonal block, the only masked one, is peeled off the loop.
+//  * The reference max is not updated block by block. Softmax is invariant to the
 //    reference (O = sum p v / sum p and LSE = m + log2 l hold for any m), so m is taken
 //    from the first key block (which holds key 0 for every query) and kept while every
 //    probability stays below 2^40. Only when a block's sum shows a larger value (a
 //    score 40 log2 units above m) does the wave recompute that block's scores, move m
 //    to the new row max and rescale l and the accumulators. This keeps the per-score
-//    max and the per-block rescale off the vector ALU, which limits this kernel at
-//    d = 64: one exp2, one fma, one add and half a convert per score remain.
+//    max and the per-block rescale off the vector ALU: one fma, one exp2, one add and
+//    half a convert per score remain.
 //  * K and V tiles go straight from global memory to LDS (global_load_lds_dwordx4, no
-//    staging registers) into a ring of three stages, two tiles ahead of the compute.
-//    A direct load writes 1 KB of consecutive LDS per instruction, so rows cannot be
-//    padded; instead the 16-byte chunks of each row are XOR-swizzled (see
-//    chunk_swizzle) so that both the 16-byte row reads of K and the transposing reads
-//    of V spread over the 64 banks.
-//  * Work order: the heaviest query blocks (the ones with the most keys) start first.
+//    staging registers) into a ring of stages, two tiles ahead of the compute; one
+//    barrier per tile. A direct load writes 1 KB of consecutive LDS per instruction, so
+//    rows cannot be padded; instead the 16-byte chunks of each row are XOR-swizzled
+//    (see chunk_swizzle) so that both the 16-byte row reads of K and the transposing
+//    reads of V spread over the 64 banks.
+//  * Work order: workgroup x runs on XCD x mod 8. When the (batch, kv head) slices
+//    split evenly over the XCDs, all query tiles of a slice go to one XCD, whose L2
+//    then serves that slice's K and V to every query head of the group; on each XCD the
+//    heaviest query tiles (the most keys) are dispatched first.
 #include "cgqa_device.hpp"
 #include "cgqa_launch.hpp"
 
+#include <stdlib.h>
 #include <string.h>
 
 #include <type_traits>
-#include <vector>
 
 namespace cgqa {
 
-template <int D, int NQB, int BN, int NW>
+template <int D>
 struct FwdCfg {
-    static constexpr int kThreads = NW * 64;
-    static constexpr int kBN = BN;                  // keys per tile
-    static constexpr int kBM = NW * 32 * NQB;       // queries per workgroup
-    static constexpr int kKD = D / 16;              // k-steps over the head dimension
-    static constexpr int kNKB = kBN / 32;           // 32-key blocks per tile
-    static constexpr int kMB = D / 32;              // 32-dim blocks of the output
-    static constexpr int kRow = D * 2;              // bytes per K or V row in LDS
-    static constexpr int kTile = kBN * kRow;        // bytes per K (or V) tile
-    static constexpr int kStages = 3;
-    static constexpr int kStage = 2 * kTile;        // K then V
+    // Query blocks of 32 per wave (the code also supports two, which halves the LDS
+    // fragment reads per product but needs ~236 registers and so at most two waves per
+    // SIMD; one block per wave allows three workgroups per CU at d = 64, which balances
+    // the causal work better and measured faster).
+    static constexpr int kNQB = 1;
+    static constexpr int kWaves = 4;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kWQ = 32 * kNQB;                   // queries per wave
+    static constexpr int kBM = kWQ * kWaves;                // queries per workgroup
+    static constexpr int kBN = 32;                          // keys per LDS tile
+    static constexpr int kBPT = kBN / 32;                   // 32-key blocks per tile
+    static constexpr int kStages = 5;
+    // Tiles issued beyond the one a barrier waits for. At the barrier for tile t the
+    // stage of tile t - 2 (kBPT = 2) or t - 3 (kBPT = 1) has been read for the last
+    // time, which leaves kStages - 2 resp. kStages - 3 stages for tiles in flight.
+    static constexpr int kAhead = kBPT == 2 ? kStages - 2 : kStages - 3;
+    static constexpr int kKD = D / 16;                      // k-steps over the head dimension
+    static constexpr int kMB = D / 32;                      // 32-dim blocks of the output
+    static constexpr int kRow = D * 2;                      // bytes per K or V row in LDS
+    static constexpr int kTile = kBN * kRow;                // bytes per K (or V) tile
+    static constexpr int kStage = 2 * kTile;                // K then V
     static constexpr int kLds = kStages * kStage;
-    static constexpr int kLoadsPerTensor = kTile / 1024 / NW;   // 1 KB per wave instruction
-    static constexpr int kLoadsPerTile = 2 * kLoadsPerTensor;    // per wave
+    static constexpr int kLoadsPerTensor = kTile / 1024 / kWaves;   // 1 KB per wave instruction
+    static constexpr int kLoadsPerTile = 2 * kLoadsPerTensor;       // per wave
     static constexpr int kRowsPerLoad = 1024 / kRow;
+    static constexpr int kUnroll = kStages * kBPT;          // period of the block -> stage map
     static_assert(D == 64 || D == 128, "head dim");
-    static_assert(kTile % (1024 * NW) == 0, "tile load must split evenly over the waves");
-    static_assert(kLds <= 160 * 1024, "LDS budget");
+    static_assert(kTile % (1024 * kWaves) == 0, "tile load must split evenly over the waves");
+    static_assert(kAhead >= 2, "prefetch distance");
+    static_assert(2 * kLds <= 160 * 1024, "two workgroups per CU");
 };
 
 // Probabilities above this trigger a move of the reference max.
 constexpr float kRescaleLimit = 1099511627776.0f;   // 2^40
 
-template <int D, int NQB, int BN, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
-    using C = FwdCfg<D, NQB, BN, NW>;
+template <int D>
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(FwdArgs a) {
+    using C = FwdCfg<D>;
+    constexpr int NQB = C::kNQB;
+    constexpr int kAll = (1 << NQB) - 1;   // bit qb: query block qb of the wave
     __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
 
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
-    const int bh_count = a.B * Hq;
-    // Task t: query tile n_qtiles-1 - t / bh_count of (batch, head) t % bh_count, so the
-    // default order starts the heaviest tiles first; small grids use the host's map.
-    const int task = a.use_map ? (int)a.task_map[blockIdx.x] : (int)blockIdx.x;
-    const int qt = a.n_qtiles - 1 - task / bh_count;
-    const int bh = task % bh_count;
-    const int b = bh / Hq, h = bh % Hq;
-    const int g = h / (Hq / Hkv);
+    const int G = Hq / Hkv;
+    int qt, b, h;
+    if (a.xcd_group) {
+        // Slices p = b * Hkv + g with p % 8 == x % 8 run on XCD x % 8 (n_pairs % 8 == 0).
+        const int xcd = (int)blockIdx.x & 7;
+        const int per_qt = (a.n_pairs >> 3) * G;
+        const int local = (int)blockIdx.x >> 3;
+        if (local >= per_qt * a.n_qtiles) return;
+        qt = a.n_qtiles - 1 - local / per_qt;
+        const int rem = local % per_qt;
+        const int p = xcd + 8 * (rem / G);
+        b = p / Hkv;
+        h = (p % Hkv) * G + rem % G;
+    } else {
+        const int bh_count = a.B * Hq;
+        qt = a.n_qtiles - 1 - (int)blockIdx.x / bh_count;
+        const int bh = (int)blockIdx.x % bh_count;
+        b = bh / Hq;
+        h = bh % Hq;
+    }
+    const int g = h / G;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // The wave index is uniform; readfirstlane lets the compiler keep everything derived
+    // from it (the wave's key range, its loop bounds) in scalar registers and branches.
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, hl = lane >> 5;
     const int q0 = qt * C::kBM;
-    const int qw = q0 + wave * 32 * NQB;   // first query of this wave
+    const int qw = q0 + C::kWQ * wave;   // first query of this wave
     const float c = a.scale_log2;
 
     const size_t q_stride = (size_t)Hq * D;     // elements between consecutive t
-    const size_t kv_stride = (size_t)Hkv * D;
+    const unsigned kv_row_bytes = (unsigned)(Hkv * D * 2);
     const uint16_t* qbase = a.q + ((size_t)b * T * Hq + h) * D;
-    const uint16_t* kbase = a.k + ((size_t)b * T * Hkv + g) * D;
-    const uint16_t* vbase = a.v + ((size_t)b * T * Hkv + g) * D;
+    const char* kbase = reinterpret_cast<const char*>(a.k + ((size_t)b * T * Hkv + g) * D);
+    const char* vbase = reinterpret_cast<const char*>(a.v + ((size_t)b * T * Hkv + g) * D);
 
-    const int kv_end = min(T, q0 + C::kBM);            // keys 0 .. kv_end-1 are needed
+    // Keys needed: up to the last query of the workgroup, with T rounded up to whole
+    // waves so that a wave's last block is always loaded (keys past T are masked for
+    // every real query).
+    const int t_pad = (T + C::kWQ - 1) / C::kWQ * C::kWQ;
+    const int kv_end = min(t_pad, q0 + C::kBM);
     const int ntiles = (kv_end + C::kBN - 1) / C::kBN;
+    const int nb_wg = (kv_end + 31) / 32;              // 32-key blocks of the workgroup
+    const bool active = qw < T;
+    const int jd = qw / 32;                            // diagonal block of query block 0
+    const int jlast = active ? jd + NQB - 1 : -1;      // the wave's last key block
 
     // Tile loader: wave instruction i of this wave fills rows
     // kRowsPerLoad * (wave * kLoadsPerTensor + i) + lane / (kRow/16) of the tile, slot
     // lane % (kRow/16), with the logical chunk that the swizzle puts there. Rows past
     // T read row T-1 (finite data; those keys are masked for every real query).
     const int ld_slot = lane % (C::kRow / 16);
-    int ld_row[C::kLoadsPerTensor], ld_chunk[C::kLoadsPerTensor];
+    int ld_row[C::kLoadsPerTensor];
+    unsigned ld_off[C::kLoadsPerTensor], ld_chunk_b[C::kLoadsPerTensor];
 #pragma unroll
     for (int i = 0; i < C::kLoadsPerTensor; ++i) {
         ld_row[i] = C::kRowsPerLoad * (wave * C::kLoadsPerTensor + i) + lane / (C::kRow / 16);
-        ld_chunk[i] = ld_slot ^ chunk_swizzle<D>(ld_row[i]);
+        ld_chunk_b[i] = (unsigned)((ld_slot ^ chunk_swizzle<D>(ld_row[i])) * 16);
+        ld_off[i] = (unsigned)ld_row[i] * kv_row_bytes + ld_chunk_b[i];
     }
-    auto issue_tile = [&](int stage, int jt) {
-        char* ks = smem + stage * C::kStage;
+    auto issue_tile = [&](int jt) CGQA_INLINE {
+        char* ks = smem + (jt % C::kStages) * C::kStage;
         char* vs = ks + C::kTile;
+        const int row0 = jt * C::kBN;
+        const size_t tbase = (size_t)row0 * kv_row_bytes;
 #pragma unroll
         for (int i = 0; i < C::kLoadsPerTensor; ++i) {
-            const int key = min(jt * C::kBN + ld_row[i], T - 1);
-            const size_t off = (size_t)key * kv_stride + ld_chunk[i] * 8;
             const int dst = (wave * C::kLoadsPerTensor + i) * 1024;
-            load_lds16(kbase + off, ks + dst);
-            load_lds16(vbase + off, vs + dst);
+            if (row0 + C::kBN <= T) {
+                load_lds16_off(kbase + tbase, ld_off[i], ks + dst);
+                load_lds16_off(vbase + tbase, ld_off[i], vs + dst);
+            } else {
+                const unsigned off = (unsigned)min(row0 + ld_row[i], T - 1) * kv_row_bytes + ld_chunk_b[i];
+                load_lds16_off(kbase, off, ks + dst);
+                load_lds16_off(vbase, off, vs + dst);
+            }
         }
     };
+    // Waits until tile t is in LDS for every wave. Tiles t+1 .. min(t+ahead, ntiles-1)
+    // may still be in flight (issued after t, so counted after it).
+    auto wait_tile = [&](int t, int ahead) CGQA_INLINE {
+        const int later = min(ahead, ntiles - 1 - t);
+        if (later >= 2) wait_tiles_barrier<2 * C::kLoadsPerTile>();
+        else if (later == 1) wait_tiles_barrier<C::kLoadsPerTile>();
+        else wait_tiles_barrier<0>();
+    };
+    // Loop head of block step j: the step that computes the scores of the first block of
+    // tile t = (j + 1) / kBPT waits for that tile and refills the stage of the oldest
+    // tile, which no wave reads any more.
+    auto head = [&](int j) CGQA_INLINE {
+        if ((j + 1) % C::kBPT != 0) return;
+        const int t = (j + 1) / C::kBPT;
+        if (t >= ntiles) return;
+        wait_tile(t, C::kAhead - 1);
+        if (t + C::kAhead < ntiles) issue_tile(t + C::kAhead);
+    };
 
-    issue_tile(0, 0);
-    if (ntiles > 1) issue_tile(1, 1);
+#pragma unroll
+    for (int t = 0; t <= C::kAhead; ++t)
+        if (t < ntiles) issue_tile(t);
 
-    // Q as the B operand: lane (query n, group hl) holds dims 16*kd + 8*hl .. +7.
+    // Q as the B operand: lane (query n of block qb, group hl) holds dims
+    // 16*kd + 8*hl .. +7.
     bf16x8 qreg[NQB][C::kKD];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -135,31 +210,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
             qreg[qb][kd] = __builtin_bit_cast(bf16x8, x);
         }
     }
-
-    // Q in registers before the loop on every path, so the compiler's waits for it do
-    // not land inside the loop (where they would also wait for the tile prefetch).
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int kd = 0; kd < C::kKD; ++kd) asm volatile("" ::"v"(qreg[qb][kd]));
 
-    f32x16 oacc[NQB][C::kMB];
-    float mref[NQB], lsum[NQB];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-        mref[qb] = 0.0f;
-        lsum[qb] = 0.0f;
-#pragma unroll
-        for (int mb = 0; mb < C::kMB; ++mb) oacc[qb][mb] = zero16();
-    }
-
     // Per-lane LDS offsets. K operand: row 32kb + n, logical chunk 2kd + hl. V operand
     // (transposing read): lane j of its 16-lane group reads row 4*hl + j/4 (+8 for the
     // second half) of a 16-row group, 8 bytes at logical column
     // 32mb + 16*((lane>>4)&1) + 4*(j%4). Rows only enter the swizzle through r % 16,
-    // which does not depend on the block, so these are per-lane constants.
-    // With the tile loop unrolled by the stage count below, every read is one of these
-    // per-lane addresses plus an immediate offset.
+    // which does not depend on the block, so these are per-lane constants; a block adds
+    // its stage and row offset as an immediate.
     const char* kaddr[C::kKD];
     const char* vaddr[C::kMB][2];
     {
@@ -176,131 +237,195 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
             for (int r = 0; r < 2; ++r)
                 vaddr[mb][r] = smem + C::kTile + (v_r0 + 8 * r) * C::kRow + v_byte + (((4 * mb + v_chunk) ^ v_swz[r]) << 4);
     }
+    // Byte offset of block j's rows (K; V adds kTile through vaddr).
+    auto block_off = [](int j) CGQA_INLINE { return ((j / C::kBPT) % C::kStages) * C::kStage + (j % C::kBPT) * 32 * C::kRow; };
 
-    for (int jt0 = 0; jt0 < ntiles; jt0 += C::kStages) {
-      static_for<C::kStages>([&](auto Uc) {
-        constexpr int U = decltype(Uc)::value;
-        constexpr int soff = U * C::kStage;
-        const int jt = jt0 + U;
-        if (jt >= ntiles) return;
-        // Tile jt is complete once at most the next tile's loads are outstanding; the
-        // barrier also tells every wave that all waves are done with tile jt - 1,
-        // whose stage the loads of tile jt + 2 reuse.
-        if (jt + 1 < ntiles) wait_tiles_barrier<C::kLoadsPerTile>();
-        else wait_tiles_barrier<0>();
-        if (jt + 2 < ntiles) issue_tile((U + 2) % C::kStages, jt + 2);
+    f32x16 oacc[NQB][C::kMB];
+    float mref[NQB], lsum[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        mref[qb] = 0.0f;
+        lsum[qb] = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < C::kMB; ++mb) oacc[qb][mb] = zero16();
+    }
 
-        const int j0 = jt * C::kBN;
+    // ---- building blocks of a step. `sel` is a bit set of query blocks.
+    auto scores = [&](int boff, int sel, f32x16 (&s)[NQB]) CGQA_INLINE {
+        bf16x8 kf[C::kKD];
+#pragma unroll
+        for (int kd = 0; kd < C::kKD; ++kd) kf[kd] = lds_read8(kaddr[kd] + boff);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+            if (sel >> qb & 1) s[qb] = mfma32x32x16(kf[0], qreg[qb][0], zero16());
+#pragma unroll
+        for (int kd = 1; kd < C::kKD; ++kd)
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+                if (sel >> qb & 1) s[qb] = mfma32x32x16(kf[kd], qreg[qb][kd], s[qb]);
+    };
+    // O^T += V^T P^T, 16 keys per instruction. B = P straight from the score registers:
+    // registers 8t..8t+7 hold keys 16t + 8*(s/4) + 4*hl + s%4 for slot s. A = the same
+    // keys of V, read transposed: slots 0..3 from rows 16t + 4*hl + r, slots 4..7 from
+    // rows 16t + 8 + 4*hl + r.
+    auto pv = [&](int boff, int sel, const bf16x8 (&pb)[NQB][2]) CGQA_INLINE {
+        bf16x8 vf[2][C::kMB];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int mb = 0; mb < C::kMB; ++mb)
+                vf[t][mb] = concat(lds_read_tr4(vaddr[mb][0] + boff + 16 * t * C::kRow),
+                                   lds_read_tr4(vaddr[mb][1] + boff + 16 * t * C::kRow));
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+                    if (sel >> qb & 1) oacc[qb][mb] = mfma32x32x16(vf[t][mb], pb[qb][t], oacc[qb][mb]);
+    };
+    // Diagonal block of query block qb (key block jd + qb): register i is key
+    // qw + 32qb + 8(i/4) + 4hl + i%4 against query qw + 32qb + n.
+    auto mask_diag = [&](f32x16& s) CGQA_INLINE {
+        const int rel = 4 * hl - n;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (rel + 8 * (i >> 2) + (i & 3) > 0) s[i] = -INFINITY;
+    };
+    auto row_max = [&](const f32x16& s) CGQA_INLINE {
+        float mx = s[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+        return max_halves(mx) * c;
+    };
+    // p = 2^(s*c - m) in place; returns this lane's sum; P rounded to bf16 for P.V.
+    auto softmax = [&](int qb, f32x16& s, bf16x8 (&pb)[2]) CGQA_INLINE {
+        const float nm = -mref[qb];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = exp2_fast(fmaf(s[i], c, nm));
+        float t0 = s[0], t1 = s[1];
+#pragma unroll
+        for (int i = 2; i < 16; i += 2) {
+            t0 += s[i];
+            t1 += s[i + 1];
+        }
+        pb[0] = pack_lo(s);
+        pb[1] = pack_hi(s);
+        return t0 + t1;
+    };
 
-        if (qw + 32 * NQB - 1 < j0) return;   // every query of this wave is before the tile
-#pragma unroll
-        for (int kb = 0; kb < C::kNKB; ++kb) {
-            const int jb = j0 + 32 * kb;
-            if (qw + 32 * NQB - 1 < jb) break;      // the rest of the tile is masked
-            // S^T = K Q^T (rows: keys, A from LDS; columns: queries), masked above the
-            // diagonal. Register i of block qb is key jb + 8(i/4) + 4hl + i%4.
-            f32x16 s[NQB];
-            const bool need_mask = (jb + 31 > qw);
-            const int koff = soff + 32 * kb * C::kRow;
-            auto scores = [&]() {
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) s[qb] = zero16();
-#pragma unroll
-                for (int kd = 0; kd < C::kKD; ++kd) {
-                    const bf16x8 ka = lds_read8(kaddr[kd] + koff);
-#pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) s[qb] = mfma32x32x16(ka, qreg[qb][kd], s[qb]);
-                }
-                if (need_mask) {
-#pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) {
-                        const int rel = jb + 4 * hl - (qw + 32 * qb + n);   // key - query at i = 0
-#pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            if (rel + 8 * (i >> 2) + (i & 3) > 0) s[qb][i] = -INFINITY;
-                    }
-                }
-            };
-            auto row_max = [&](int qb) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][i]);
-                mx = fmaxf(mx, swap_halves(mx));
-                return mx * c;
-            };
-            float tsum[NQB];
-            auto exponentials = [&]() {
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) {
-                    tsum[qb] = 0.0f;
-                    const float nm = -mref[qb];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float p = exp2_fast(fmaf(s[qb][i], c, nm));
-                        s[qb][i] = p;
-                        tsum[qb] += p;
-                    }
-                }
-            };
+    f32x16 s_cur[NQB];
+    bf16x8 p_prev[NQB][2];
 
-            scores();
-            if (jb == 0) {
-                // Key 0 is in this block for every query: a finite reference max.
+    // One step j: scores of block j+1 for the query blocks in NX, P.V of block j-1 for
+    // those in PV, softmax of block j for those in SM (masked for those in DG). The
+    // matrix-core work depends on neither softmax, so the two interleave.
+    auto step = [&](int koff_next, int voff_prev, int koff_cur, auto PVc, auto SMc, auto DGc, auto NXc) CGQA_INLINE {
+        constexpr int PV = decltype(PVc)::value, SM = decltype(SMc)::value;
+        constexpr int DG = decltype(DGc)::value, NX = decltype(NXc)::value;
+        f32x16 s_nx[NQB];
+        bf16x8 p_cur[NQB][2];
+        float t[NQB];
+        if constexpr (NX != 0) scores(koff_next, NX, s_nx);
+        if constexpr (PV != 0) pv(voff_prev, PV, p_prev);
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) mref[qb] = row_max(qb);
-            }
-            exponentials();
-            bool big = false;
+        for (int qb = 0; qb < NQB; ++qb) {
+            if (!(SM >> qb & 1)) continue;
+            if (DG >> qb & 1) mask_diag(s_cur[qb]);
+            t[qb] = softmax(qb, s_cur[qb], p_cur[qb]);
+        }
+        // Code-generation workaround, measured: this empty unrolled loop keeps the
+        // compiler from merging the products and the softmax with the rare-path check
+        // below; without it the step takes 12 more registers, 40 more copies and ~10%
+        // longer. (An asm statement or sched_barrier here does not have the effect.)
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) big |= !(tsum[qb] <= kRescaleLimit);
-            if (wave_any(big)) {
-                // Rare: some score rose far above the reference. Recompute the block's
-                // scores, move the reference to the row max and rescale what was
-                // summed so far.
-                scores();
+        for (int i = 0; i < 8; ++i) {
+        }
+        bool big = false;
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) {
-                    const float mnew = fmaxf(mref[qb], row_max(qb));
-                    const float alpha = exp2_fast(mref[qb] - mnew);
-                    mref[qb] = mnew;
-                    lsum[qb] *= alpha;
+        for (int qb = 0; qb < NQB; ++qb)
+            if (SM >> qb & 1) big |= !(t[qb] <= kRescaleLimit);
+        if (wave_any(big)) {
+            // Rare: some score rose far above the reference. Recompute the block's
+            // scores, move the reference to the row max and rescale what was summed so
+            // far.
+            f32x16 s2[NQB];
+            scores(koff_cur, SM, s2);
 #pragma unroll
-                    for (int mb = 0; mb < C::kMB; ++mb)
+            for (int qb = 0; qb < NQB; ++qb) {
+                if (!(SM >> qb & 1)) continue;
+                if (DG >> qb & 1) mask_diag(s2[qb]);
+                const float mnew = fmaxf(mref[qb], row_max(s2[qb]));
+                const float alpha = exp2_fast(mref[qb] - mnew);
+                mref[qb] = mnew;
+                lsum[qb] *= alpha;
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) oacc[qb][mb][i] *= alpha;
-                }
-                exponentials();
-            }
+                for (int mb = 0; mb < C::kMB; ++mb)
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) lsum[qb] += tsum[qb];
-
-            // O^T += V^T P^T, 16 keys per instruction. B = P straight from the score
-            // registers: registers 8t..8t+7 hold keys 16t + 8*(s/4) + 4*hl + s%4 for
-            // slot s. A = the same keys of V, read transposed: slots 0..3 from rows
-            // 16t + 4*hl + r, slots 4..7 from rows 16t + 8 + 4*hl + r.
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                bf16x8 pb[NQB];
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) pb[qb] = t == 0 ? pack_lo(s[qb]) : pack_hi(s[qb]);
-                const int voff = soff + (32 * kb + 16 * t) * C::kRow;
-#pragma unroll
-                for (int mb = 0; mb < C::kMB; ++mb) {
-                    const bf16x8 va = concat(lds_read_tr4(vaddr[mb][0] + voff), lds_read_tr4(vaddr[mb][1] + voff));
-#pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) oacc[qb][mb] = mfma32x32x16(va, pb[qb], oacc[qb][mb]);
-                }
+                    for (int i = 0; i < 16; ++i) oacc[qb][mb][i] *= alpha;
+                s_cur[qb] = s2[qb];
+                t[qb] = softmax(qb, s_cur[qb], p_cur[qb]);
             }
         }
-      });
-    }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            if (SM >> qb & 1) {
+                lsum[qb] += t[qb];
+                p_prev[qb][0] = p_cur[qb][0];
+                p_prev[qb][1] = p_cur[qb][1];
+            }
+            if (NX >> qb & 1) s_cur[qb] = s_nx[qb];
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using IAll = std::integral_constant<int, kAll>;
+
+        // the matrix core beside the softmax of block j.
+        // ---- prologue: tile 0, scores of block 0 and the reference maximum.
+        wait_tile(0, C::kAhead);
+        if (active) {
+            scores(0, kAll, s_cur);
+            f32x16 sm = s_cur[0];
+            if (jd == 0) mask_diag(sm);
+            mref[0] = row_max(sm);
+        }
+        if (active && jd >= 1) {
+            // Step 0: no P.V yet.
+            head(0);
+            step(block_off(1), 0, block_off(0), I0{}, IAll{}, I0{}, IAll{});
+            // Steady steps 1 .. jd-1, unrolled by the period of the stage map so that
+            // every LDS address is a per-lane register plus an immediate.
+            for (int j0 = 0; j0 < jd; j0 += C::kUnroll) {
+                static_for<C::kUnroll>([&](auto Uc) CGQA_INLINE {
+                    constexpr int U = decltype(Uc)::value;
+                    const int j = j0 + U;
+                    if (j == 0 || j >= jd) return;
+                    if constexpr ((U + 1) % C::kBPT == 0) head(j);
+                    constexpr int off_next = block_off((U + 1) % C::kUnroll);
+                    constexpr int off_cur = block_off(U);
+                    constexpr int off_prev = block_off((U + C::kUnroll - 1) % C::kUnroll);
+                    step(off_next, off_prev, off_cur, IAll{}, IAll{}, I0{}, IAll{});
+                });
+            }
+        }
+        if (active) {
+            // Step jd: the diagonal block, then its own P.V.
+            head(jd);
+            if (jd >= 1)
+                step(0, block_off(jd - 1), block_off(jd), IAll{}, IAll{}, IAll{}, I0{});
+            else
+                step(0, 0, block_off(jd), I0{}, IAll{}, IAll{}, I0{});
+            pv(block_off(jd), kAll, p_prev);
+        }
+    // Steps after this wave's last block: keep the workgroup's barriers and loads going.
+    for (int j = jlast + 1; j < nb_wg; ++j) head(j);
 
     // ---- epilogue: O = acc / l in bf16, LSE = ln2 * (m + log2 l).
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
         const int query = qw + 32 * qb + n;
-        const float l = lsum[qb] + swap_halves(lsum[qb]);
-        if (query >= T) continue;
+        if (!active || query >= T) continue;
+        const float l = sum_halves(lsum[qb]);
         const float inv = 1.0f / l;
         uint16_t* orow = a.o + ((size_t)b * T + query) * q_stride + (size_t)h * D;
 #pragma unroll
@@ -318,63 +443,26 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     }
 }
 
-// Balanced placement for grids of at most three workgroups per CU. All of them are
-// resident at once, and the dispatcher places workgroup x on CU x mod n_cu (measured on
-// MI355X: x, x + 256 and x + 512 share a CU). A task's load is proportional to its
-// number of key tiles, n_qtiles - t / bh_count; the longest tasks are dealt first,
-// each to the least loaded CU with a free slot. A different placement only costs
-// balance, never correctness.
-static bool build_task_map(int blocks, int bh_count, int n_qtiles, int n_cu, uint16_t* map) {
-    if (n_cu <= 0 || blocks > kFwdMaxMapped || blocks > 3 * n_cu || blocks <= n_cu) return false;
-    struct Cache { int blocks = -1, bh = -1, nq = -1, ncu = -1; uint16_t map[kFwdMaxMapped]; };
-    thread_local Cache cache;
-    if (cache.blocks == blocks && cache.bh == bh_count && cache.nq == n_qtiles && cache.ncu == n_cu) {
-        memcpy(map, cache.map, sizeof(uint16_t) * blocks);
-        return true;
-    }
-    std::vector<int> load(n_cu, 0), used(n_cu, 0);
-    // Tasks are already in decreasing load order (t increases as the tile gets lighter).
-    for (int t = 0; t < blocks; ++t) {
-        const int w = n_qtiles - t / bh_count;
-        int best = -1;
-        for (int c = 0; c < n_cu; ++c) {
-            if (c + used[c] * n_cu >= blocks) continue;   // no free slot on this CU
-            if (best < 0 || load[c] < load[best]) best = c;
-        }
-        map[best + used[best] * n_cu] = (uint16_t)t;
-        ++used[best];
-        load[best] += w;
-    }
-    cache.blocks = blocks;
-    cache.bh = bh_count;
-    cache.nq = n_qtiles;
-    cache.ncu = n_cu;
-    memcpy(cache.map, map, sizeof(uint16_t) * blocks);
-    return true;
-}
-
-static int device_cu_count() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    return n;
-}
-
-template <int D, int NQB, int BN, int NW>
+template <int D>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-    using C = FwdCfg<D, NQB, BN, NW>;
+    using C = FwdCfg<D>;
     FwdArgs x = a;
     x.n_qtiles = (a.T + C::kBM - 1) / C::kBM;
+    x.n_pairs = a.B * a.Hkv;
+    x.xcd_group = x.n_pairs % 8 == 0 ? 1 : 0;
     const long blocks = (long)x.n_qtiles * a.B * a.Hq;
-    x.use_map = blocks <= kFwdMaxMapped &&
-                build_task_map((int)blocks, a.B * a.Hq, x.n_qtiles, device_cu_count(), x.task_map);
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NQB, BN, NW>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, x);
+    hipLaunchKernelGGL((attn_fwd_kernel<D>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, x);
     return hipGetLastError();
 }
 
+// Forward kernel choice: the tiled kernel above. The balanced kernel
+// (attn_fwd_split.hip) is parity-tested but slower on every measured workload, so it
+// runs only when CGQA_FWD_KERNEL=split asks for it on a shape it supports.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-    if (a.d == 64) return launch_fwd_t<64, 1, 64, 4>(a, stream);
-    return launch_fwd_t<128, 1, 32, 4>(a, stream);
+    const char* force = getenv("CGQA_FWD_KERNEL");
+    if (force && strcmp(force, "split") == 0 && fwd_split_supported(a)) return launch_fwd_split(a, stream);
+    if (a.d == 64) return launch_fwd_t<64>(a, stream);
+    return launch_fwd_t<128>(a, stream);
 }
 
 }  // namespace cgqa

@@ -118,6 +118,21 @@ __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_lo
 // Value held by the lane 32 positions away (the other k-group of the same column).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
+// x of lane l combined with x of lane l ^ 32 through v_permlane32_swap (no LDS). Both
+// lanes of a pair add (or compare) the low-half value first, so they get the same bits.
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Kernel-local lambdas capture the kernel's register arrays by reference; they must be
+// inlined, or those arrays would move to scratch memory.
+#define CGQA_INLINE __attribute__((always_inline))
+
 // Instruction-scheduling hints for a basic block (groups are filled in order).
 constexpr int kSchedVALU = 0x002;
 constexpr int kSchedMFMA = 0x008;

@@ -6,10 +6,6 @@
 
 namespace cgqa {
 
-// Largest grid the forward launcher balances with an explicit task map: three rounds
-// of workgroups on 256 CUs (all resident at once).
-constexpr int kFwdMaxMapped = 768;
-
 struct FwdArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -18,9 +14,9 @@ struct FwdArgs {
     float* lse;
     int B, T, Hq, Hkv, d;
     float scale_log2;   // scale * log2(e): scores in log2 units
-    int n_qtiles;       // set by the launcher
-    int use_map;        // set by the launcher: task of workgroup x is task_map[x]
-    uint16_t task_map[kFwdMaxMapped];
+    int n_qtiles;       // set by the launcher: query tiles per (batch, head)
+    int n_pairs;        // set by the launcher: B * Hkv (batch, kv head) slices
+    int xcd_group;      // set by the launcher: keep each slice's tiles on one XCD
 };
 
 struct BwdArgs {
@@ -42,6 +38,10 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// Balanced forward for d = 64 and whole 64-query blocks (attn_fwd_split.hip).
+bool fwd_split_supported(const FwdArgs& a);
+long fwd_split_blocks(const FwdArgs& a);
+hipError_t launch_fwd_split(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkv(const BwdArgs& a, hipStream_t stream);
 
