@@ -240,7 +240,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
                 else tile(Uc, std::false_type{}, j0);
             }
             if (jt + 1 < ntiles) store_tile(1 - U);
-            __syncthreads();
+            lds_barrier();
         });
     }
 
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- sum the head slots (ascending) and store: one 32-dim block of dK, then of dV,
     // at a time through the same LDS area; every wave's lane values line up across
@@ -531,7 +531,7 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
                         *reinterpret_cast<f32x4*>(mine + 4 * u) = x;
                     }
                 }
-                __syncthreads();
+                lds_barrier();
                 if (hs == 0) {
 #pragma unroll
                     for (int s2 = 1; s2 < HS; ++s2) {
@@ -544,7 +544,7 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
                         }
                     }
                 }
-                __syncthreads();
+                lds_barrier();
             }
             if (hs == 0 && key < T) {
                 float* row = out + kvoff + (size_t)key * kv_stride;

@@ -259,6 +259,13 @@ __device__ __forceinline__ void wait_tiles_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for
+// its global loads and stores (which __syncthreads() would drain too), then joins the
+// barrier. Enough when the barrier only orders LDS writes before LDS reads.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
