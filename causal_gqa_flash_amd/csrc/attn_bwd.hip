@@ -284,7 +284,6 @@ struct DkvCfg {
     static constexpr int kThreads = NKW * HS * 64;
     static constexpr int kKD = D / 16;
     static constexpr int kMB = D / 32;
-    static constexpr int kQSB = BQ / 32;           // 32-query blocks per staged tile
     // Raw ring (NR stages, filled by DMA two steps ahead when NR = 3): Q and dO rows as
     // bf16, then lse and delta as fp32.
     static constexpr int kRawRow = D * 2;
@@ -306,7 +305,7 @@ struct DkvCfg {
     static constexpr int kRedBytes = NKW * (HS - 1) * 64 * 16 * 4;
     static constexpr int kLds = (HS * kSlot > kRedBytes) ? HS * kSlot : kRedBytes;
     static_assert(D == 64 || D == 128, "head dim");
-    static_assert(BQ % 32 == 0, "query tile");
+    static_assert(BQ == 32, "one 32-query block per step");
     static_assert(NR == 2 || NR == 3, "raw ring depth");
     static_assert(kRawTile % (1024 * NKW) == 0, "tile DMA must split evenly over a slot");
     static_assert(kStatLanes >= 1 && kStatLanes <= 64 && (2 * BQ) % NKW == 0, "stat DMA lanes");
@@ -329,7 +328,8 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     const int b = bg / Hkv, g = bg % Hkv;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hs = wave / NKW;                     // head slot
     const int kwr = wave % NKW;                    // wave index within the slot
     const int pos = (kwr + hs) % NKW;              // key-block position within the workgroup
@@ -350,30 +350,6 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     const size_t kv_stride = (size_t)Hkv * D;
     const size_t kvoff = ((size_t)b * T * Hkv + g) * D;
 
-    // K and V of the lane's key as B operands (dims 16*kd + 8*hl .. +7), in fp16.
-    f16x8 kreg[C::kKD], vreg[C::kKD];
-#pragma unroll
-    for (int kd = 0; kd < C::kKD; ++kd) {
-        u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-        if (key < T) {
-            const size_t off = kvoff + (size_t)key * kv_stride + 16 * kd + 8 * hl;
-            xk = load16(a.k + off);
-            xv = load16(a.v + off);
-        }
-        kreg[kd] = bf16x8_to_f16(xk);
-        vreg[kd] = bf16x8_to_f16(xv);
-    }
-
-    // K and V in registers before the loop on every path, so the compiler's waits for
-    // them stay out of the loop (there they would also wait for the DMA prefetch, which
-    // the compiler does not track).
-#pragma unroll
-    for (int kd = 0; kd < C::kKD; ++kd) asm volatile("" ::"v"(kreg[kd]), "v"(vreg[kd]));
-
-    f32x16 dkacc[C::kMB], dvacc[C::kMB];
-#pragma unroll
-    for (int mb = 0; mb < C::kMB; ++mb) { dkacc[mb] = zero16(); dvacc[mb] = zero16(); }
-
     // Steps of a slot: its heads ascending, then query tiles ascending from the tile
     // holding the workgroup's earliest key. Every slot has the same number of steps
     // (HS divides G).
@@ -384,42 +360,86 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     const int nsteps = kb_first < nkb ? heads_per_slot * per_head : 0;
 
     char* slot_base = smem + hs * C::kSlot;
-    auto raw_stage = [&](int st) { return slot_base + (st % NR) * C::kRawStage; };
     auto conv_stage = [&](int st) { return slot_base + NR * C::kRawStage + (st & 1) * C::kConvStage; };
-    auto step_head = [&](int st) { return g * G + hs + HS * (st / per_head); };
-    auto step_q0 = [&](int st) { return (qt_begin + st % per_head) * BQ; };
+    // A step's head, first query and raw ring stage, advanced one step at a time (the
+    // DMA and the conversion each keep one, for the next step they handle).
+    struct Cursor {
+        int h, q0, stage;
+        size_t row;      // element offset of the step's first Q / dO row
+        size_t stat;     // element offset of the step's first lse / delta value
+    };
+    auto head_start = [&](Cursor& c, int h) CGQA_INLINE {
+        c.h = h;
+        c.q0 = qt_begin * BQ;
+        c.row = (((size_t)b * T + c.q0) * Hq + h) * D;
+        c.stat = ((size_t)b * Hq + h) * T + c.q0;
+    };
+    auto advance = [&](Cursor& c) CGQA_INLINE {
+        c.q0 += BQ;
+        c.row += (size_t)BQ * q_stride;
+        c.stat += BQ;
+        if (c.q0 >= nqt * BQ) head_start(c, c.h + HS);
+        c.stage = c.stage + 1 == NR ? 0 : c.stage + 1;
+    };
+    Cursor dma_cur;
+    dma_cur.stage = 0;
+    head_start(dma_cur, g * G + hs);
+    Cursor cvt_cur = dma_cur;
 
     // DMA of one step into the raw ring: each wave of the slot copies kTileLoads KB of
     // Q rows and of dO rows (row-major, 1 KB per instruction), and kStatLanes floats of
-    // lse / delta (4 bytes per lane). Query rows past T read row T-1; the conversion
-    // masks them.
-    auto issue_step = [&](int st) {
-        char* raw = raw_stage(st);
-        const int h = step_head(st);
-        const int qs0 = step_q0(st);
-        const size_t hoff = ((size_t)b * T * Hq + h) * D;
+    // lse / delta (4 bytes per lane), from a wave-uniform base (the step's first row)
+    // plus constant lane offsets. Query rows past T read row T-1; the conversion masks
+    // them.
+    const unsigned lds0 = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)smem);
+    const unsigned q_row_bytes = (unsigned)q_stride * 2u;
+    int dma_row[C::kTileLoads];
+    unsigned dma_col[C::kTileLoads], dma_off[C::kTileLoads];
+#pragma unroll
+    for (int i = 0; i < C::kTileLoads; ++i) {
+        const int byte = (kwr * C::kTileLoads + i) * 1024 + 16 * lane;
+        dma_row[i] = byte / C::kRawRow;
+        dma_col[i] = (unsigned)(byte % C::kRawRow);
+        dma_off[i] = (unsigned)dma_row[i] * q_row_bytes + dma_col[i];
+    }
+    const bool stat_lse = kwr * C::kStatLanes < BQ;          // wave-uniform: lse or delta
+    const int stat_row = (kwr * C::kStatLanes + lane) % BQ;
+    auto issue_step = [&]() CGQA_INLINE {
+        const unsigned raw = lds0 + (unsigned)(slot_base - smem) + dma_cur.stage * C::kRawStage;
+        const int qs0 = dma_cur.q0;
+        const int last = T - 1 - qs0;                        // rows past it repeat row T-1
+        unsigned off[C::kTileLoads];
+        if (qs0 + BQ <= T) {
+#pragma unroll
+            for (int i = 0; i < C::kTileLoads; ++i) off[i] = dma_off[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::kTileLoads; ++i)
+                off[i] = (unsigned)min(dma_row[i], last) * q_row_bytes + dma_col[i];
+        }
+        // One instruction per chunk, each with its own (never negative) lane offset: the
+        // 32-bit offset is zero-extended, so an offset reduced by a later chunk's
+        // instruction offset could wrap when a ragged tile clamps its rows.
+        const unsigned lds = raw + kwr * C::kTileLoads * 1024;
 #pragma unroll
         for (int i = 0; i < C::kTileLoads; ++i) {
-            const int ci = kwr * C::kTileLoads + i;              // 1 KB chunk of the tile
-            const int byte = ci * 1024 + 16 * lane;
-            const int row = byte / C::kRawRow, col = (byte % C::kRawRow) / 16;
-            const int query = min(qs0 + row, T - 1);
-            const size_t off = hoff + (size_t)query * q_stride + col * 8;
-            load_lds16(a.q + off, raw + ci * 1024);
-            load_lds16(a.dO + off, raw + C::kRawTile + ci * 1024);
+            const unsigned o1[1] = {off[i]};
+            load_lds16_chunks<1>(a.q + dma_cur.row, o1, lds + 1024 * i);
+            load_lds16_chunks<1>(a.dO + dma_cur.row, o1, lds + C::kRawTile + 1024 * i);
         }
         if (lane < C::kStatLanes) {
-            const int f = kwr * C::kStatLanes + lane;            // float index in lse|delta
-            const int query = min(qs0 + (f % BQ), T - 1);
-            const float* src = (f < BQ ? a.lse : a.delta) + ((size_t)b * Hq + h) * T + query;
-            load_lds4(src, raw + 2 * C::kRawTile + kwr * C::kStatLanes * 4);
+            const float* sb = (stat_lse ? a.lse : a.delta) + dma_cur.stat;
+            load_lds4_off(sb, (unsigned)min(stat_row, last) * 4u, raw + 2 * C::kRawTile + kwr * C::kStatLanes * 4);
         }
+        advance(dma_cur);
     };
     // Raw step -> converted step (fp16 rows, scaled and masked statistics).
-    auto convert_step = [&](int st) {
-        const char* raw = raw_stage(st);
+    auto convert_step = [&](int st) CGQA_INLINE {
+        const char* raw = slot_base + cvt_cur.stage * C::kRawStage;
         char* cv = conv_stage(st);
-        const int qs0 = step_q0(st);
+        const int qs0 = cvt_cur.q0;
+        advance(cvt_cur);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -439,76 +459,121 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
             reinterpret_cast<float*>(cv + 2 * C::kTile)[stid] = y;
         }
     };
-    auto wait_barrier = [&](int pending_steps) {
+    auto wait_barrier = [&](int pending_steps) CGQA_INLINE {
         // pending_steps: how many of this wave's issued steps may still be in flight.
         if (pending_steps <= 0) wait_tiles_barrier<0>();
         else if (pending_steps == 1) wait_tiles_barrier<C::kVmPerStep>();
         else wait_tiles_barrier<2 * C::kVmPerStep>();
     };
 
-    // Prologue: DMA the first NR steps, convert step 0.
-    for (int st = 0; st < NR && st < nsteps; ++st) issue_step(st);
+    // Prologue: DMA the first NR steps, then load K and V of the lane's key as B
+    // operands (dims 16*kd + 8*hl .. +7) in fp16, so the two latencies overlap.
+    for (int st = 0; st < NR && st < nsteps; ++st) issue_step();
+    f16x8 kreg[C::kKD], vreg[C::kKD];
+#pragma unroll
+    for (int kd = 0; kd < C::kKD; ++kd) {
+        u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+        if (key < T) {
+            const size_t off = kvoff + (size_t)key * kv_stride + 16 * kd + 8 * hl;
+            xk = load16(a.k + off);
+            xv = load16(a.v + off);
+        }
+        kreg[kd] = bf16x8_to_f16(xk);
+        vreg[kd] = bf16x8_to_f16(xv);
+    }
+    // K and V in registers before the loop on every path, so the compiler's waits for
+    // them stay out of the loop (there they would also wait for the DMA prefetch, which
+    // the compiler does not track).
+#pragma unroll
+    for (int kd = 0; kd < C::kKD; ++kd) asm volatile("" ::"v"(kreg[kd]), "v"(vreg[kd]));
+
+    f32x16 dkacc[C::kMB], dvacc[C::kMB];
+#pragma unroll
+    for (int mb = 0; mb < C::kMB; ++mb) { dkacc[mb] = zero16(); dvacc[mb] = zero16(); }
+
     wait_barrier(min(NR, nsteps) - 1);
     if (nsteps > 0) convert_step(0);
 
     const int tr_row = (lane & 15) >> 2;
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    for (int step = 0; step < nsteps; ++step) {
+    // One 32-query block of a step against the wave's keys. The causal mask is needed
+    // only on the wave's diagonal block (first query = first key): MASK is a
+    // compile-time flag so that the other blocks carry no comparisons.
+    auto block = [&](auto Mc, const char* qs, const char* ds, const float* lse2s, const float* dels, int sb) CGQA_INLINE {
+        constexpr bool MASK = decltype(Mc)::value;
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int kd = 0; kd < C::kKD; ++kd) {
+            const int off = (32 * sb + n) * C::kPitch + (16 * kd + 8 * hl) * 2;
+            s = mfma32x32x16(lds_read8_f16(qs + off), kreg[kd], s);
+            dp = mfma32x32x16(lds_read8_f16(ds + off), vreg[kd], dp);
+        }
+        // Register i holds query 8*(i/4) + 4*hl + i%4 of the block, of the lane's key.
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = 32 * sb + 8 * u + 4 * hl;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + r);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dels + r);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * u + e;
+                float p = exp2_fast(fmaf(s[i], a.scale_log2, -l4[e]));
+                if constexpr (MASK)
+                    if (n > 8 * u + 4 * hl + e) p = 0.0f;      // key after query
+                s[i] = p;
+                dp[i] = p * (dp[i] - d4[e]);           // dS
+            }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per instruction.
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const f16x8 pb = t == 0 ? pack_lo_f16(s) : pack_hi_f16(s);
+            const f16x8 sb8 = t == 0 ? pack_lo_f16(dp) : pack_hi_f16(dp);
+            const int r0 = 32 * sb + 16 * t + 4 * hl + tr_row;
+#pragma unroll
+            for (int mb = 0; mb < C::kMB; ++mb) {
+                const int off = r0 * C::kPitch + (32 * mb + tr_col) * 2;
+                const f16x8 dot = concat(lds_read_tr4_f16(ds + off), lds_read_tr4_f16(ds + off + 8 * C::kPitch));
+                const f16x8 qt8 = concat(lds_read_tr4_f16(qs + off), lds_read_tr4_f16(qs + off + 8 * C::kPitch));
+                dvacc[mb] = mfma32x32x16(dot, pb, dvacc[mb]);
+                dkacc[mb] = mfma32x32x16(qt8, sb8, dkacc[mb]);
+            }
+        }
+    };
+
+    // Step `step` of the slot: wait for its data (and retire the stages that the next
+    // DMA and conversion reuse), start the DMA three steps ahead, convert the next step.
+    auto sync_step = [&](int step) CGQA_INLINE {
         // Step+1 complete in LDS (only newer steps may be in flight); the barrier also
         // retires every wave's use of the stages that the next DMA and conversion reuse.
         wait_barrier(min(step + NR - 1, nsteps - 1) - (step + 1));
-        if (step + NR < nsteps) issue_step(step + NR);
+        if (step + NR < nsteps) issue_step();
         if (step + 1 < nsteps) convert_step(step + 1);
-
+    };
+    auto compute_step = [&](auto Mc, int step) CGQA_INLINE {
         const char* qs = conv_stage(step);
         const char* ds = qs + C::kTile;
         const float* lse2s = reinterpret_cast<const float*>(ds + C::kTile);
-        const float* dels = lse2s + BQ;
-        const int qs0 = step_q0(step);
-
-#pragma unroll
-        for (int sb = 0; sb < C::kQSB; ++sb) {
-            const int qb0 = qs0 + 32 * sb;             // first query of this block
-            if (qb0 + 31 < kwb) continue;              // every query precedes every key
-            f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-            for (int kd = 0; kd < C::kKD; ++kd) {
-                const int off = (32 * sb + n) * C::kPitch + (16 * kd + 8 * hl) * 2;
-                s = mfma32x32x16(lds_read8_f16(qs + off), kreg[kd], s);
-                dp = mfma32x32x16(lds_read8_f16(ds + off), vreg[kd], dp);
-            }
-            // Register i holds query qb0 + 8*(i/4) + 4*hl + i%4 of the lane's key.
-            const bool need_mask = (qb0 < kwb + 31);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int r = 32 * sb + 8 * u + 4 * hl;
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + r);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dels + r);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * u + e;
-                    float p = exp2_fast(fmaf(s[i], a.scale_log2, -l4[e]));
-                    if (need_mask && key > qb0 + 8 * u + 4 * hl + e) p = 0.0f;
-                    s[i] = p;
-                    dp[i] = p * (dp[i] - d4[e]);           // dS
-                }
-            }
-            // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per instruction.
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const f16x8 pb = t == 0 ? pack_lo_f16(s) : pack_hi_f16(s);
-                const f16x8 sb8 = t == 0 ? pack_lo_f16(dp) : pack_hi_f16(dp);
-                const int r0 = 32 * sb + 16 * t + 4 * hl + tr_row;
-#pragma unroll
-                for (int mb = 0; mb < C::kMB; ++mb) {
-                    const int off = r0 * C::kPitch + (32 * mb + tr_col) * 2;
-                    const f16x8 dot = concat(lds_read_tr4_f16(ds + off), lds_read_tr4_f16(ds + off + 8 * C::kPitch));
-                    const f16x8 qt8 = concat(lds_read_tr4_f16(qs + off), lds_read_tr4_f16(qs + off + 8 * C::kPitch));
-                    dvacc[mb] = mfma32x32x16(dot, pb, dvacc[mb]);
-                    dkacc[mb] = mfma32x32x16(qt8, sb8, dkacc[mb]);
-                }
-            }
+        block(Mc, qs, ds, lse2s, lse2s + BQ, 0);
+    };
+    // Each head pass of the slot: the steps before the wave's diagonal block (queries
+    // that precede all its keys: loads and conversions only), the diagonal step (with
+    // the mask), then the rest. Waves without a block only keep the loads going.
+    const int diag = kwb < T ? kwb / 32 - qt_begin : per_head;   // diagonal step within a pass
+    for (int hp = 0; hp < heads_per_slot; ++hp) {
+        const int s0 = hp * per_head, s1 = s0 + per_head;
+        const int sd = min(s0 + diag, s1);
+        int step = s0;
+        for (; step < sd; ++step) sync_step(step);
+        if (step < s1) {
+            sync_step(step);
+            compute_step(std::true_type{}, step);
+            ++step;
+        }
+        for (; step < s1; ++step) {
+            sync_step(step);
+            compute_step(std::false_type{}, step);
         }
     }
     lds_barrier();

@@ -222,6 +222,18 @@ __device__ __forceinline__ void load_lds4(const void* src, const void* lds_base)
         : "memory");
 }
 
+// load_lds4 with the address split into a wave-uniform base and a 32-bit lane offset
+// (bytes); lds is the wave-uniform LDS byte address.
+__device__ __forceinline__ void load_lds4_off(const void* base, unsigned off, unsigned lds) {
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)base);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)((uintptr_t)base >> 32));
+    const uint64_t sbase = lo | (hi << 32);
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds);
+    unsigned saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(off), "s"(m0), "s"(sbase) : "memory");
+}
+
 // Physical 16-byte slot of logical chunk c in LDS row r is c ^ chunk_swizzle<D>(r) for
 // tiles written by direct-to-LDS loads (whose rows cannot be padded). LDS serves 64
 // banks x 4 bytes per clock: a D=64 row (128 B) is half a bank window, a D=128 row a
