@@ -466,9 +466,10 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
         else wait_tiles_barrier<2 * C::kVmPerStep>();
     };
 
-    // Prologue: DMA the first NR steps, then load K and V of the lane's key as B
-    // operands (dims 16*kd + 8*hl .. +7) in fp16, so the two latencies overlap.
-    for (int st = 0; st < NR && st < nsteps; ++st) issue_step();
+    // Prologue: DMA step 0, then load K and V of the lane's key as B operands (dims
+    // 16*kd + 8*hl .. +7) in fp16, so the two latencies overlap; only these are waited
+    // for before the later steps are issued.
+    if (nsteps > 0) issue_step();
     f16x8 kreg[C::kKD], vreg[C::kKD];
 #pragma unroll
     for (int kd = 0; kd < C::kKD; ++kd) {
@@ -491,7 +492,8 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
 #pragma unroll
     for (int mb = 0; mb < C::kMB; ++mb) { dkacc[mb] = zero16(); dvacc[mb] = zero16(); }
 
-    wait_barrier(min(NR, nsteps) - 1);
+    wait_tiles_barrier<0>();
+    for (int st = 1; st < NR && st < nsteps; ++st) issue_step();
     if (nsteps > 0) convert_step(0);
 
     const int tr_row = (lane & 15) >> 2;
@@ -543,12 +545,18 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     };
 
     // Step `step` of the slot: wait for its data (and retire the stages that the next
-    // DMA and conversion reuse), start the DMA three steps ahead, convert the next step.
+    // DMA and conversion reuse) and start the DMA NR steps ahead. The next step is
+    // converted after this step's products are issued (convert_next), so that the
+    // conversion's LDS round trip overlaps the matrix core instead of delaying the
+    // operand reads: its raw stage is complete at this barrier, its fp16 stage was
+    // last read before it, and the next barrier publishes it.
     auto sync_step = [&](int step) CGQA_INLINE {
         // Step+1 complete in LDS (only newer steps may be in flight); the barrier also
         // retires every wave's use of the stages that the next DMA and conversion reuse.
         wait_barrier(min(step + NR - 1, nsteps - 1) - (step + 1));
         if (step + NR < nsteps) issue_step();
+    };
+    auto convert_next = [&](int step) CGQA_INLINE {
         if (step + 1 < nsteps) convert_step(step + 1);
     };
     auto compute_step = [&](auto Mc, int step) CGQA_INLINE {
@@ -565,45 +573,50 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
         const int s0 = hp * per_head, s1 = s0 + per_head;
         const int sd = min(s0 + diag, s1);
         int step = s0;
-        for (; step < sd; ++step) sync_step(step);
+        for (; step < sd; ++step) {
+            sync_step(step);
+            convert_next(step);
+        }
         if (step < s1) {
             sync_step(step);
             compute_step(std::true_type{}, step);
+            convert_next(step);
             ++step;
         }
         for (; step < s1; ++step) {
             sync_step(step);
             compute_step(std::false_type{}, step);
+            convert_next(step);
         }
     }
     lds_barrier();
 
     // ---- sum the head slots (ascending) and store: one 32-dim block of dK, then of dV,
     // at a time through the same LDS area; every wave's lane values line up across
-    // slots.
+    // slots. A wave's block is stored as four groups of 64 lanes x 16 bytes, so each
+    // 16-byte access of a wave covers 1 KB of consecutive LDS (no bank conflicts).
     float* red = reinterpret_cast<float*>(smem);
+    auto red_at = [&](int slot, int u) { return red + (size_t)((((slot - 1) * NKW + pos) * 4 + u) * 64 + lane) * 4; };
     auto reduce_store = [&](f32x16 (&acc)[C::kMB], float* out, float mul) {
 #pragma unroll
         for (int mb = 0; mb < C::kMB; ++mb) {
             if (HS > 1) {
                 if (hs > 0) {
-                    float* mine = red + (size_t)(((hs - 1) * NKW + pos) * 64 + lane) * 16;
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         f32x4 x;
 #pragma unroll
                         for (int r = 0; r < 4; ++r) x[r] = acc[mb][4 * u + r];
-                        *reinterpret_cast<f32x4*>(mine + 4 * u) = x;
+                        *reinterpret_cast<f32x4*>(red_at(hs, u)) = x;
                     }
                 }
                 lds_barrier();
                 if (hs == 0) {
 #pragma unroll
                     for (int s2 = 1; s2 < HS; ++s2) {
-                        const float* src = red + (size_t)(((s2 - 1) * NKW + pos) * 64 + lane) * 16;
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
-                            const f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * u);
+                            const f32x4 x = *reinterpret_cast<const f32x4*>(red_at(s2, u));
 #pragma unroll
                             for (int r = 0; r < 4; ++r) acc[mb][4 * u + r] += x[r];
                         }
