@@ -31,6 +31,12 @@ SMALL = [
     (1, 257, 12, 4, 64, 11, 1.0),
     (2, 300, 4, 1, 128, 12, 1.0),
     (1, 1000, 6, 2, 64, 13, 1.0),
+    # every dK/dV launch variant at d = 64: G = 2 (two head slots), G = 6 (three slots of
+    # two heads), G = 8 (four slots of two waves, two heads each); and d = 128 with G = 3
+    (2, 161, 4, 2, 64, 14, 1.0),
+    (1, 96, 6, 1, 64, 15, 2.0),
+    (1, 130, 8, 1, 64, 16, 1.0),
+    (2, 77, 6, 2, 128, 17, 1.0),
 ]
 
 
