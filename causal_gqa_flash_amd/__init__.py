@@ -10,6 +10,8 @@ from ._binding import (  # noqa: F401
     CGQA_EHIP,
     CGQA_EINVAL,
     CGQA_EUNSUPPORTED,
+    CGQA_GRAD_BF16,
+    CGQA_GRAD_F32,
     CGQA_OK,
     CgqaError,
     attn_bwd_dkv,

@@ -10,6 +10,8 @@ CGQA_OK = 0
 CGQA_EINVAL = 1
 CGQA_EUNSUPPORTED = 2
 CGQA_EHIP = 3
+CGQA_GRAD_F32 = 0
+CGQA_GRAD_BF16 = 1
 
 _lib = None
 
@@ -43,6 +45,12 @@ def library():
         lib.attn_bwd_dq.restype = i
         lib.attn_bwd_dkv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.attn_bwd_dkv.restype = i
+        lib.attn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+        lib.attn_fwd_strided.restype = i
+        lib.attn_bwd_dq_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i, f, vp]
+        lib.attn_bwd_dq_strided.restype = i
+        lib.attn_bwd_dkv_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, vp]
+        lib.attn_bwd_dkv_strided.restype = i
         lib.attn_status_string.argtypes = [i]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.cgqa_last_hip_error.argtypes = []
@@ -74,18 +82,30 @@ def _stream_ptr(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _need(t, name, dtype, shape):
+def _need(t, name, dtype, shape, rows=False):
+    """Checks a tensor's type, shape and device. With rows=True a [B, T, H, d] tensor may
+    be a view whose tokens sit every rs elements (strides (T*rs, rs, d, 1), rs >= H*d);
+    returns rs (H*d for a contiguous tensor)."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != dtype:
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
+    if t.is_contiguous():
+        return shape[2] * shape[3] if rows else None
+    if not rows:
         raise ValueError(f"{name} must be contiguous")
+    B, T, H, d = shape
+    st = t.stride()
+    rs = st[1] if T > 1 else (st[0] if B > 1 else H * d)
+    ok = st[3] == 1 and (H == 1 or st[2] == d) and (B == 1 or T == 1 or st[0] == T * st[1]) and rs >= H * d
+    if not ok:
+        raise ValueError(f"{name} must be [B, T, H, d] with strides (T*rs, rs, d, 1), got {st}")
+    return rs
 
 
 def _dims(q, k):
@@ -103,62 +123,98 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _kv_stride(rk, rv):
+    if rk != rv:
+        raise ValueError(f"k and v must share one row stride, got {rk} and {rv}")
+    return rk
+
+
 def attn_fwd(q, k, v, scale=None, o=None, lse=None, stream=None):
-    """o [B,T,Hq,d] bf16 and lse [B,Hq,T] fp32 for bf16 q [B,T,Hq,d], k, v [B,T,Hkv,d]."""
+    """o [B,T,Hq,d] bf16 and lse [B,Hq,T] fp32 for bf16 q [B,T,Hq,d], k, v [B,T,Hkv,d].
+    q, k, v and o may be row-strided views (e.g. of one packed QKV buffer)."""
     torch = _torch()
     B, T, Hq, Hkv, d = _dims(q, k)
-    _need(q, "q", torch.bfloat16, (B, T, Hq, d))
-    _need(k, "k", torch.bfloat16, (B, T, Hkv, d))
-    _need(v, "v", torch.bfloat16, (B, T, Hkv, d))
+    rq = _need(q, "q", torch.bfloat16, (B, T, Hq, d), rows=True)
+    rkv = _kv_stride(_need(k, "k", torch.bfloat16, (B, T, Hkv, d), rows=True),
+                     _need(v, "v", torch.bfloat16, (B, T, Hkv, d), rows=True))
     if o is None:
-        o = torch.empty_like(q)
+        o = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
-    _need(o, "o", torch.bfloat16, (B, T, Hq, d))
+    ro = _need(o, "o", torch.bfloat16, (B, T, Hq, d), rows=True)
     _need(lse, "lse", torch.float32, (B, Hq, T))
-    _check("attn_fwd", library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                          B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
+    lib = library()
+    if (rq, rkv, ro) == (Hq * d, Hkv * d, Hq * d):
+        _check("attn_fwd", lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                        B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
+    else:
+        _check("attn_fwd_strided", lib.attn_fwd_strided(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq, Hkv, d, rq, rkv, ro,
+            _scale(scale, d), _stream_ptr(stream)))
     return o, lse
 
 
-def attn_bwd_dq(q, k, v, o, do, lse, scale=None, delta=None, dq=None, stream=None):
-    """delta [B,Hq,T] fp32 and dq [B,T,Hq,d] fp32."""
+def _grad_code(dtype):
+    torch = _torch()
+    return CGQA_GRAD_BF16 if dtype == torch.bfloat16 else CGQA_GRAD_F32
+
+
+def attn_bwd_dq(q, k, v, o, do, lse, scale=None, delta=None, dq=None, stream=None, grad_dtype=None):
+    """delta [B,Hq,T] fp32 and dq [B,T,Hq,d], fp32 or bf16 (the dtype of the dq given,
+    else grad_dtype, else fp32). Inputs and dq may be row-strided views."""
     torch = _torch()
     B, T, Hq, Hkv, d = _dims(q, k)
-    for t, name in ((q, "q"), (o, "o"), (do, "do")):
-        _need(t, name, torch.bfloat16, (B, T, Hq, d))
-    _need(k, "k", torch.bfloat16, (B, T, Hkv, d))
-    _need(v, "v", torch.bfloat16, (B, T, Hkv, d))
+    rq, ro, rdo = (_need(t, name, torch.bfloat16, (B, T, Hq, d), rows=True)
+                   for t, name in ((q, "q"), (o, "o"), (do, "do")))
+    rkv = _kv_stride(_need(k, "k", torch.bfloat16, (B, T, Hkv, d), rows=True),
+                     _need(v, "v", torch.bfloat16, (B, T, Hkv, d), rows=True))
     _need(lse, "lse", torch.float32, (B, Hq, T))
     if delta is None:
         delta = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
     if dq is None:
-        dq = torch.empty((B, T, Hq, d), dtype=torch.float32, device=q.device)
+        dq = torch.empty((B, T, Hq, d), dtype=grad_dtype or torch.float32, device=q.device)
     _need(delta, "delta", torch.float32, (B, Hq, T))
-    _need(dq, "dq", torch.float32, (B, T, Hq, d))
-    _check("attn_bwd_dq", library().attn_bwd_dq(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq),
-        B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
+    rdq = _need(dq, "dq", (torch.float32, torch.bfloat16), (B, T, Hq, d), rows=True)
+    lib = library()
+    if (rq, rkv, ro, rdo, rdq) == (Hq * d, Hkv * d, Hq * d, Hq * d, Hq * d) and dq.dtype == torch.float32:
+        _check("attn_bwd_dq", lib.attn_bwd_dq(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq),
+            B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
+    else:
+        _check("attn_bwd_dq_strided", lib.attn_bwd_dq_strided(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq),
+            B, T, Hq, Hkv, d, rq, rkv, ro, rdo, rdq, _grad_code(dq.dtype), _scale(scale, d), _stream_ptr(stream)))
     return delta, dq
 
 
-def attn_bwd_dkv(q, k, v, do, lse, delta, scale=None, dk=None, dv=None, stream=None):
-    """dk, dv [B,T,Hkv,d] fp32. Enqueue after attn_bwd_dq on the same stream."""
+def attn_bwd_dkv(q, k, v, do, lse, delta, scale=None, dk=None, dv=None, stream=None, grad_dtype=None):
+    """dk, dv [B,T,Hkv,d], fp32 or bf16 (the dtype of the dk/dv given, else grad_dtype,
+    else fp32). Enqueue after attn_bwd_dq on the same stream. Inputs and dk, dv may be
+    row-strided views (dk and dv with one row stride)."""
     torch = _torch()
     B, T, Hq, Hkv, d = _dims(q, k)
-    for t, name in ((q, "q"), (do, "do")):
-        _need(t, name, torch.bfloat16, (B, T, Hq, d))
-    _need(k, "k", torch.bfloat16, (B, T, Hkv, d))
-    _need(v, "v", torch.bfloat16, (B, T, Hkv, d))
+    rq, rdo = (_need(t, name, torch.bfloat16, (B, T, Hq, d), rows=True) for t, name in ((q, "q"), (do, "do")))
+    rkv = _kv_stride(_need(k, "k", torch.bfloat16, (B, T, Hkv, d), rows=True),
+                     _need(v, "v", torch.bfloat16, (B, T, Hkv, d), rows=True))
     _need(lse, "lse", torch.float32, (B, Hq, T))
     _need(delta, "delta", torch.float32, (B, Hq, T))
     if dk is None:
-        dk = torch.empty((B, T, Hkv, d), dtype=torch.float32, device=q.device)
+        dk = torch.empty((B, T, Hkv, d), dtype=grad_dtype or torch.float32, device=q.device)
     if dv is None:
-        dv = torch.empty((B, T, Hkv, d), dtype=torch.float32, device=q.device)
-    _need(dk, "dk", torch.float32, (B, T, Hkv, d))
-    _need(dv, "dv", torch.float32, (B, T, Hkv, d))
-    _check("attn_bwd_dkv", library().attn_bwd_dkv(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
-        B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
+        dv = torch.empty((B, T, Hkv, d), dtype=dk.dtype, device=q.device)
+    if dk.dtype != dv.dtype:
+        raise TypeError(f"dk and dv must have one dtype, got {dk.dtype} and {dv.dtype}")
+    rdk = _need(dk, "dk", (torch.float32, torch.bfloat16), (B, T, Hkv, d), rows=True)
+    rdv = _need(dv, "dv", (torch.float32, torch.bfloat16), (B, T, Hkv, d), rows=True)
+    if rdk != rdv:
+        raise ValueError(f"dk and dv must share one row stride, got {rdk} and {rdv}")
+    lib = library()
+    if (rq, rkv, rdo, rdk) == (Hq * d, Hkv * d, Hq * d, Hkv * d) and dk.dtype == torch.float32:
+        _check("attn_bwd_dkv", lib.attn_bwd_dkv(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
+            B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
+    else:
+        _check("attn_bwd_dkv_strided", lib.attn_bwd_dkv_strided(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
+            B, T, Hq, Hkv, d, rq, rkv, rdo, rdk, _grad_code(dk.dtype), _scale(scale, d), _stream_ptr(stream)))
     return dk, dv

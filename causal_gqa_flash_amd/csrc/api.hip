@@ -12,25 +12,49 @@ thread_local int g_last_hip_error = 0;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-struct Span {
-    uintptr_t lo, hi;   // [lo, hi)
+// A tensor as the kernels address it: `rows` rows (B*T tokens) of `width` elements
+// (H*d) every `rs` elements, `eb` bytes per element.
+struct View {
+    const void* p;
+    int64_t rows, width, rs, eb;
+    uintptr_t lo() const { return (uintptr_t)p; }
+    uintptr_t hi() const { return (uintptr_t)p + (uintptr_t)(((rows - 1) * rs + width) * eb); }
 };
-Span span(const void* p, int64_t elems, int64_t elem_bytes) {
-    return Span{(uintptr_t)p, (uintptr_t)p + (uintptr_t)(elems * elem_bytes)};
-}
-bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 
-// Shape checks shared by the three calls. Returns CGQA_OK, or sets *empty for B or T = 0.
+// True if no element of a lies in b. Tensors whose byte ranges meet must have the same
+// row pitch and column windows that do not intersect within a row (interleaved heads of
+// one packed buffer); any other meeting ranges count as overlapping.
+bool disjoint(View a, View b) {
+    if (a.hi() <= b.lo() || b.hi() <= a.lo()) return true;
+    if (a.rs * a.eb != b.rs * b.eb) return false;
+    if (a.lo() > b.lo()) {
+        View t = a;
+        a = b;
+        b = t;
+    }
+    const uint64_t pitch = (uint64_t)(a.rs * a.eb);
+    const uint64_t k = (uint64_t)(b.lo() - a.lo()) % pitch;   // b's first byte within a row of a
+    return k >= (uint64_t)(a.width * a.eb) && k + (uint64_t)(b.width * b.eb) <= pitch;
+}
+
+// Shape checks shared by the calls. Returns CGQA_OK, or sets *empty for B or T = 0.
 int check_shape(int B, int T, int Hq, int Hkv, int d, float scale, bool* empty) {
     *empty = false;
     if (B < 0 || T < 0 || Hq < 1 || Hkv < 1) return CGQA_EINVAL;
     if (Hq % Hkv != 0) return CGQA_EINVAL;
     if (!(scale > 0.0f) || !isfinite(scale)) return CGQA_EINVAL;
     if (d != 64 && d != 128) return CGQA_EUNSUPPORTED;
-    // Every element count must stay below 2^31 (kernel grids and row indices are int).
-    const int64_t n_q = (int64_t)B * T * Hq * d;
-    if (n_q >= ((int64_t)1 << 31)) return CGQA_EINVAL;
+    if ((int64_t)B * Hq * T >= ((int64_t)1 << 31)) return CGQA_EINVAL;
     if (B == 0 || T == 0) *empty = true;
+    return CGQA_OK;
+}
+
+// A row stride of a tensor with `width` elements per row: at least the row, at most
+// 2^31 elements in all (kernel offsets are 32-bit within a tensor's rows), and a
+// multiple of `align` elements (whole 16- or 8-byte accesses).
+int check_stride(int64_t rs, int64_t width, int64_t rows, int64_t align) {
+    if (rs < width || rows * rs >= ((int64_t)1 << 31)) return CGQA_EINVAL;
+    if (rs % align != 0) return CGQA_EUNSUPPORTED;
     return CGQA_OK;
 }
 
@@ -42,86 +66,152 @@ int finish(hipError_t e) {
     return CGQA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
-             int B, int T, int Hq, int Hkv, int d, float scale, void* stream) {
+int fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+             int B, int T, int Hq, int Hkv, int d, int q_rs, int kv_rs, int o_rs, float scale, void* stream) {
     bool empty = false;
     int rc = check_shape(B, T, Hq, Hkv, d, scale, &empty);
-    if (rc != CGQA_OK || empty) return rc;
+    if (rc != CGQA_OK) return rc;
+    const int64_t rows = (int64_t)B * T, wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d;
+    const int64_t rcs[3] = {check_stride(q_rs, wq, rows, 8), check_stride(kv_rs, wkv, rows, 8),
+                            check_stride(o_rs, wq, rows, 4)};
+    for (int64_t r : rcs)
+        if (r == CGQA_EINVAL) return CGQA_EINVAL;
+    for (int64_t r : rcs)
+        if (r != CGQA_OK) return (int)r;
+    if (empty) return CGQA_OK;
     if (!q || !k || !v || !o || !lse) return CGQA_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
         return CGQA_EUNSUPPORTED;
-    const int64_t nq = (int64_t)B * T * Hq * d, nkv = (int64_t)B * T * Hkv * d, nr = (int64_t)B * Hq * T;
-    const Span so = span(o, nq, 2), sl = span(lse, nr, 4);
-    const Span ins[3] = {span(q, nq, 2), span(k, nkv, 2), span(v, nkv, 2)};
-    if (overlap(so, sl)) return CGQA_EINVAL;
-    for (const Span& s : ins)
-        if (overlap(s, so) || overlap(s, sl)) return CGQA_EINVAL;
+    const View vo{o, rows, wq, o_rs, 2}, vl{lse, 1, (int64_t)B * Hq * T, (int64_t)B * Hq * T, 4};
+    const View ins[3] = {View{q, rows, wq, q_rs, 2}, View{k, rows, wkv, kv_rs, 2}, View{v, rows, wkv, kv_rs, 2}};
+    if (!disjoint(vo, vl)) return CGQA_EINVAL;
+    for (const View& s : ins)
+        if (!disjoint(s, vo) || !disjoint(s, vl)) return CGQA_EINVAL;
 
     cgqa::FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
     a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+    a.q_rs = q_rs; a.kv_rs = kv_rs; a.o_rs = o_rs;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
     return finish(cgqa::launch_fwd(a, (hipStream_t)stream));
 }
 
-static int bwd_common(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
-                      const uint16_t* dO, const float* lse, const float* delta_in, float* delta_out,
-                      float* dq, float* dk, float* dv, int B, int T, int Hq, int Hkv, int d, float scale,
-                      void* stream, bool is_dq) {
+struct BwdStrides {
+    int q_rs, kv_rs, o_rs, do_rs, dq_rs, dkv_rs, grad;
+};
+
+int bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+             const uint16_t* dO, const float* lse, const float* delta_in, float* delta_out,
+             void* dq, void* dk, void* dv, int B, int T, int Hq, int Hkv, int d, const BwdStrides& st,
+             float scale, void* stream, bool is_dq) {
     bool empty = false;
     int rc = check_shape(B, T, Hq, Hkv, d, scale, &empty);
-    if (rc != CGQA_OK || empty) return rc;
-    const int64_t nq = (int64_t)B * T * Hq * d, nkv = (int64_t)B * T * Hkv * d, nr = (int64_t)B * Hq * T;
+    if (rc != CGQA_OK) return rc;
+    if (st.grad != CGQA_GRAD_F32 && st.grad != CGQA_GRAD_BF16) return CGQA_EINVAL;
+    const int64_t rows = (int64_t)B * T, wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d, nr = (int64_t)B * Hq * T;
+    const int64_t geb = st.grad == CGQA_GRAD_BF16 ? 2 : 4;
+    int64_t rcs[4] = {check_stride(st.q_rs, wq, rows, 8), check_stride(st.kv_rs, wkv, rows, 8),
+                      check_stride(st.do_rs, wq, rows, 8),
+                      is_dq ? check_stride(st.dq_rs, wq, rows, 4) : check_stride(st.dkv_rs, wkv, rows, 4)};
+    const int64_t rco = is_dq ? check_stride(st.o_rs, wq, rows, 8) : CGQA_OK;
+    for (int64_t r : rcs)
+        if (r == CGQA_EINVAL) return CGQA_EINVAL;
+    if (rco == CGQA_EINVAL) return CGQA_EINVAL;
+    for (int64_t r : rcs)
+        if (r != CGQA_OK) return (int)r;
+    if (rco != CGQA_OK) return (int)rco;
+    if (empty) return CGQA_OK;
+    const View vq{q, rows, wq, st.q_rs, 2}, vk{k, rows, wkv, st.kv_rs, 2}, vv{v, rows, wkv, st.kv_rs, 2},
+        vdo{dO, rows, wq, st.do_rs, 2}, vl{lse, 1, nr, nr, 4};
     if (is_dq) {
         if (!q || !k || !v || !o || !dO || !lse || !delta_out || !dq) return CGQA_EINVAL;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
             !aligned16(lse) || !aligned16(delta_out) || !aligned16(dq))
             return CGQA_EUNSUPPORTED;
-        const Span outs[2] = {span(delta_out, nr, 4), span(dq, nq, 4)};
-        const Span ins[6] = {span(q, nq, 2), span(k, nkv, 2), span(v, nkv, 2),
-                             span(o, nq, 2), span(dO, nq, 2), span(lse, nr, 4)};
-        if (overlap(outs[0], outs[1])) return CGQA_EINVAL;
-        for (const Span& s : ins)
-            if (overlap(s, outs[0]) || overlap(s, outs[1])) return CGQA_EINVAL;
+        const View outs[2] = {View{delta_out, 1, nr, nr, 4}, View{dq, rows, wq, st.dq_rs, geb}};
+        const View ins[6] = {vq, vk, vv, View{o, rows, wq, st.o_rs, 2}, vdo, vl};
+        if (!disjoint(outs[0], outs[1])) return CGQA_EINVAL;
+        for (const View& s : ins)
+            if (!disjoint(s, outs[0]) || !disjoint(s, outs[1])) return CGQA_EINVAL;
     } else {
         if (!q || !k || !v || !dO || !lse || !delta_in || !dk || !dv) return CGQA_EINVAL;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) ||
             !aligned16(delta_in) || !aligned16(dk) || !aligned16(dv))
             return CGQA_EUNSUPPORTED;
-        const Span outs[2] = {span(dk, nkv, 4), span(dv, nkv, 4)};
-        const Span ins[6] = {span(q, nq, 2), span(k, nkv, 2), span(v, nkv, 2),
-                             span(dO, nq, 2), span(lse, nr, 4), span(delta_in, nr, 4)};
-        if (overlap(outs[0], outs[1])) return CGQA_EINVAL;
-        for (const Span& s : ins)
-            if (overlap(s, outs[0]) || overlap(s, outs[1])) return CGQA_EINVAL;
+        const View outs[2] = {View{dk, rows, wkv, st.dkv_rs, geb}, View{dv, rows, wkv, st.dkv_rs, geb}};
+        const View ins[6] = {vq, vk, vv, vdo, vl, View{delta_in, 1, nr, nr, 4}};
+        if (!disjoint(outs[0], outs[1])) return CGQA_EINVAL;
+        for (const View& s : ins)
+            if (!disjoint(s, outs[0]) || !disjoint(s, outs[1])) return CGQA_EINVAL;
     }
     cgqa::BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
     a.delta = is_dq ? delta_out : const_cast<float*>(delta_in);
     a.dq = dq; a.dk = dk; a.dv = dv;
     a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+    a.q_rs = st.q_rs; a.kv_rs = st.kv_rs; a.o_rs = st.o_rs; a.do_rs = st.do_rs;
+    a.dq_rs = st.dq_rs; a.dkv_rs = st.dkv_rs; a.grad_bf16 = st.grad == CGQA_GRAD_BF16 ? 1 : 0;
     a.scale = scale;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
     return finish(is_dq ? cgqa::launch_bwd_dq(a, (hipStream_t)stream)
                         : cgqa::launch_bwd_dkv(a, (hipStream_t)stream));
 }
 
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+             int B, int T, int Hq, int Hkv, int d, float scale, void* stream) {
+    // Contiguous strides; a product that overflows int is caught by the shape check.
+    const int64_t wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d;
+    if (Hq < 1 || Hkv < 1 || wq >= ((int64_t)1 << 31)) return CGQA_EINVAL;
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, d, (int)wq, (int)wkv, (int)wq, scale, stream);
+}
+
+int attn_fwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                     int B, int T, int Hq, int Hkv, int d, int q_row_stride, int kv_row_stride,
+                     int o_row_stride, float scale, void* stream) {
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, d, q_row_stride, kv_row_stride, o_row_stride, scale, stream);
+}
+
 int attn_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                 const uint16_t* dO, const float* lse, float* delta, float* dq,
                 int B, int T, int Hq, int Hkv, int d, float scale, void* stream) {
-    return bwd_common(q, k, v, o, dO, lse, nullptr, delta, dq, nullptr, nullptr, B, T, Hq, Hkv, d,
-                      scale, stream, true);
+    const int64_t wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d;
+    if (Hq < 1 || Hkv < 1 || wq >= ((int64_t)1 << 31)) return CGQA_EINVAL;
+    const BwdStrides st{(int)wq, (int)wkv, (int)wq, (int)wq, (int)wq, (int)wkv, CGQA_GRAD_F32};
+    return bwd_impl(q, k, v, o, dO, lse, nullptr, delta, dq, nullptr, nullptr, B, T, Hq, Hkv, d, st, scale,
+                    stream, true);
 }
 
 int attn_bwd_dkv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
                  const float* lse, const float* delta, float* dk, float* dv,
                  int B, int T, int Hq, int Hkv, int d, float scale, void* stream) {
-    return bwd_common(q, k, v, nullptr, dO, lse, delta, nullptr, nullptr, dk, dv, B, T, Hq, Hkv, d,
-                      scale, stream, false);
+    const int64_t wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d;
+    if (Hq < 1 || Hkv < 1 || wq >= ((int64_t)1 << 31)) return CGQA_EINVAL;
+    const BwdStrides st{(int)wq, (int)wkv, (int)wq, (int)wq, (int)wq, (int)wkv, CGQA_GRAD_F32};
+    return bwd_impl(q, k, v, nullptr, dO, lse, delta, nullptr, nullptr, dk, dv, B, T, Hq, Hkv, d, st, scale,
+                    stream, false);
+}
+
+int attn_bwd_dq_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                        const uint16_t* dO, const float* lse, float* delta, void* dq,
+                        int B, int T, int Hq, int Hkv, int d, int q_row_stride, int kv_row_stride,
+                        int o_row_stride, int do_row_stride, int dq_row_stride, int grad_dtype,
+                        float scale, void* stream) {
+    const BwdStrides st{q_row_stride, kv_row_stride, o_row_stride, do_row_stride, dq_row_stride, 0, grad_dtype};
+    return bwd_impl(q, k, v, o, dO, lse, nullptr, delta, dq, nullptr, nullptr, B, T, Hq, Hkv, d, st, scale,
+                    stream, true);
+}
+
+int attn_bwd_dkv_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
+                         const float* lse, const float* delta, void* dk, void* dv,
+                         int B, int T, int Hq, int Hkv, int d, int q_row_stride, int kv_row_stride,
+                         int do_row_stride, int dkv_row_stride, int grad_dtype, float scale, void* stream) {
+    const BwdStrides st{q_row_stride, kv_row_stride, 0, do_row_stride, 0, dkv_row_stride, grad_dtype};
+    return bwd_impl(q, k, v, nullptr, dO, lse, delta, nullptr, nullptr, dk, dv, B, T, Hq, Hkv, d, st, scale,
+                    stream, false);
 }
 
 const char* attn_status_string(int status) {

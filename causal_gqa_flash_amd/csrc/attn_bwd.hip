@@ -75,11 +75,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     const int q0 = qt * C::kBM;
     const int qw = q0 + wave * 32 * NQB;
 
-    const size_t q_stride = (size_t)Hq * D;
-    const size_t kv_stride = (size_t)Hkv * D;
-    const size_t qoff = ((size_t)b * T * Hq + h) * D;
-    const uint16_t* kbase = a.k + ((size_t)b * T * Hkv + g) * D;
-    const uint16_t* vbase = a.v + ((size_t)b * T * Hkv + g) * D;
+    const size_t kv_stride = (size_t)a.kv_rs;
+    const uint16_t* qrow0 = a.q + (size_t)b * T * a.q_rs + (size_t)h * D;
+    const uint16_t* dorow0 = a.dO + (size_t)b * T * a.do_rs + (size_t)h * D;
+    const uint16_t* orow0 = a.o + (size_t)b * T * a.o_rs + (size_t)h * D;
+    const uint16_t* kbase = a.k + (size_t)b * T * a.kv_rs + (size_t)g * D;
+    const uint16_t* vbase = a.v + (size_t)b * T * a.kv_rs + (size_t)g * D;
 
     // Q (fp16) and dO (bf16, as given) as B operands (lane: query n, dims 16*kd + 8*hl
     // .. +7), D~ and LSE. dP = V dO^T multiplies inputs only, so it runs in bf16
@@ -95,10 +96,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
         for (int kd = 0; kd < C::kKD; ++kd) {
             u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u}, xo = {0u, 0u, 0u, 0u};
             if (row < T) {
-                const size_t off = qoff + (size_t)row * q_stride + 16 * kd + 8 * hl;
-                xq = load16(a.q + off);
-                xd = load16(a.dO + off);
-                xo = load16(a.o + off);
+                const int col = 16 * kd + 8 * hl;
+                xq = load16(qrow0 + (size_t)row * a.q_rs + col);
+                xd = load16(dorow0 + (size_t)row * a.do_rs + col);
+                xo = load16(orow0 + (size_t)row * a.o_rs + col);
             }
             qreg[qb][kd] = bf16x8_to_f16(xq);
             doreg[qb][kd] = __builtin_bit_cast(bf16x8, xd);
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
         if (query >= T) continue;
         if (hl == 0) a.delta[((size_t)b * Hq + h) * T + query] = dfull;
         const float corr = dfull - dtilde[qb];
-        float* drow = a.dq + qoff + (size_t)query * q_stride;
+        const size_t drow = ((size_t)b * T + query) * a.dq_rs + (size_t)h * D;
 #pragma unroll
         for (int mb = 0; mb < C::kMB; ++mb)
 #pragma unroll
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     x[r] = a.scale * fmaf(-corr, kbar[qb][mb][4 * u + r], dqacc[qb][mb][4 * u + r]);
-                *reinterpret_cast<f32x4*>(drow + 32 * mb + 8 * u + 4 * hl) = x;
+                store_out4(a.dq, drow + 32 * mb + 8 * u + 4 * hl, x, a.grad_bf16);
             }
     }
 }
@@ -314,7 +315,11 @@ struct DkvCfg {
     static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
-template <int D, int BQ, int NKW, int HS, int NR>
+// SAME_QDO: Q and dO have the same row stride (every contiguous call), so their DMA
+// shares one set of lane offsets and one cursor offset. BF16OUT: dK and dV are written
+// as bf16 (a compile-time choice: a run-time one costs this kernel registers it has not
+// got).
+template <int D, int BQ, int NKW, int HS, int NR, bool SAME_QDO, bool BF16OUT>
 __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) {
     using C = DkvCfg<D, BQ, NKW, HS, NR>;
     __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
@@ -346,10 +351,6 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     const int kwb = gp < nkb ? 32 * block_at(gp) : T;     // first key of this wave (T: none)
     const int key = kwb + n;                       // this lane's key (column)
 
-    const size_t q_stride = (size_t)Hq * D;
-    const size_t kv_stride = (size_t)Hkv * D;
-    const size_t kvoff = ((size_t)b * T * Hkv + g) * D;
-
     // Steps of a slot: its heads ascending, then query tiles ascending from the tile
     // holding the workgroup's earliest key. Every slot has the same number of steps
     // (HS divides G).
@@ -365,18 +366,20 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     // DMA and the conversion each keep one, for the next step they handle).
     struct Cursor {
         int h, q0, stage;
-        size_t row;      // element offset of the step's first Q / dO row
-        size_t stat;     // element offset of the step's first lse / delta value
+        size_t row, row_do;   // element offsets of the step's first Q and dO rows
+        size_t stat;          // element offset of the step's first lse / delta value
     };
     auto head_start = [&](Cursor& c, int h) CGQA_INLINE {
         c.h = h;
         c.q0 = qt_begin * BQ;
-        c.row = (((size_t)b * T + c.q0) * Hq + h) * D;
+        c.row = ((size_t)b * T + c.q0) * a.q_rs + (size_t)h * D;
+        if constexpr (!SAME_QDO) c.row_do = ((size_t)b * T + c.q0) * a.do_rs + (size_t)h * D;
         c.stat = ((size_t)b * Hq + h) * T + c.q0;
     };
     auto advance = [&](Cursor& c) CGQA_INLINE {
         c.q0 += BQ;
-        c.row += (size_t)BQ * q_stride;
+        c.row += (size_t)BQ * a.q_rs;
+        if constexpr (!SAME_QDO) c.row_do += (size_t)BQ * a.do_rs;
         c.stat += BQ;
         if (c.q0 >= nqt * BQ) head_start(c, c.h + HS);
         c.stage = c.stage + 1 == NR ? 0 : c.stage + 1;
@@ -393,15 +396,16 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     // them.
     const unsigned lds0 = __builtin_amdgcn_readfirstlane(
         (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)smem);
-    const unsigned q_row_bytes = (unsigned)q_stride * 2u;
+    const unsigned q_row_bytes = (unsigned)a.q_rs * 2u, do_row_bytes = (unsigned)a.do_rs * 2u;
     int dma_row[C::kTileLoads];
-    unsigned dma_col[C::kTileLoads], dma_off[C::kTileLoads];
+    unsigned dma_col[C::kTileLoads], dma_off[C::kTileLoads], dma_off_do[C::kTileLoads];
 #pragma unroll
     for (int i = 0; i < C::kTileLoads; ++i) {
         const int byte = (kwr * C::kTileLoads + i) * 1024 + 16 * lane;
         dma_row[i] = byte / C::kRawRow;
         dma_col[i] = (unsigned)(byte % C::kRawRow);
         dma_off[i] = (unsigned)dma_row[i] * q_row_bytes + dma_col[i];
+        dma_off_do[i] = SAME_QDO ? dma_off[i] : (unsigned)dma_row[i] * do_row_bytes + dma_col[i];
     }
     const bool stat_lse = kwr * C::kStatLanes < BQ;          // wave-uniform: lse or delta
     const int stat_row = (kwr * C::kStatLanes + lane) % BQ;
@@ -409,14 +413,20 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
         const unsigned raw = lds0 + (unsigned)(slot_base - smem) + dma_cur.stage * C::kRawStage;
         const int qs0 = dma_cur.q0;
         const int last = T - 1 - qs0;                        // rows past it repeat row T-1
-        unsigned off[C::kTileLoads];
+        unsigned off[C::kTileLoads], off_do[C::kTileLoads];
         if (qs0 + BQ <= T) {
 #pragma unroll
-            for (int i = 0; i < C::kTileLoads; ++i) off[i] = dma_off[i];
+            for (int i = 0; i < C::kTileLoads; ++i) {
+                off[i] = dma_off[i];
+                off_do[i] = SAME_QDO ? dma_off[i] : dma_off_do[i];
+            }
         } else {
 #pragma unroll
-            for (int i = 0; i < C::kTileLoads; ++i)
-                off[i] = (unsigned)min(dma_row[i], last) * q_row_bytes + dma_col[i];
+            for (int i = 0; i < C::kTileLoads; ++i) {
+                const unsigned r = (unsigned)min(dma_row[i], last);
+                off[i] = r * q_row_bytes + dma_col[i];
+                off_do[i] = SAME_QDO ? off[i] : r * do_row_bytes + dma_col[i];
+            }
         }
         // One instruction per chunk, each with its own (never negative) lane offset: the
         // 32-bit offset is zero-extended, so an offset reduced by a later chunk's
@@ -424,9 +434,9 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
         const unsigned lds = raw + kwr * C::kTileLoads * 1024;
 #pragma unroll
         for (int i = 0; i < C::kTileLoads; ++i) {
-            const unsigned o1[1] = {off[i]};
+            const unsigned o1[1] = {off[i]}, o2[1] = {off_do[i]};
             load_lds16_chunks<1>(a.q + dma_cur.row, o1, lds + 1024 * i);
-            load_lds16_chunks<1>(a.dO + dma_cur.row, o1, lds + C::kRawTile + 1024 * i);
+            load_lds16_chunks<1>(a.dO + (SAME_QDO ? dma_cur.row : dma_cur.row_do), o2, lds + C::kRawTile + 1024 * i);
         }
         if (lane < C::kStatLanes) {
             const float* sb = (stat_lse ? a.lse : a.delta) + dma_cur.stat;
@@ -475,7 +485,7 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     for (int kd = 0; kd < C::kKD; ++kd) {
         u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
         if (key < T) {
-            const size_t off = kvoff + (size_t)key * kv_stride + 16 * kd + 8 * hl;
+            const size_t off = ((size_t)b * T + key) * a.kv_rs + (size_t)g * D + 16 * kd + 8 * hl;
             xk = load16(a.k + off);
             xv = load16(a.v + off);
         }
@@ -597,7 +607,7 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     // 16-byte access of a wave covers 1 KB of consecutive LDS (no bank conflicts).
     float* red = reinterpret_cast<float*>(smem);
     auto red_at = [&](int slot, int u) { return red + (size_t)((((slot - 1) * NKW + pos) * 4 + u) * 64 + lane) * 4; };
-    auto reduce_store = [&](f32x16 (&acc)[C::kMB], float* out, float mul) {
+    auto reduce_store = [&](f32x16 (&acc)[C::kMB], void* out, float mul) {
 #pragma unroll
         for (int mb = 0; mb < C::kMB; ++mb) {
             if (HS > 1) {
@@ -625,13 +635,13 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
                 lds_barrier();
             }
             if (hs == 0 && key < T) {
-                float* row = out + kvoff + (size_t)key * kv_stride;
+                const size_t row = ((size_t)b * T + key) * a.dkv_rs + (size_t)g * D;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     f32x4 x;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) x[r] = acc[mb][4 * u + r] * mul;
-                    *reinterpret_cast<f32x4*>(row + 32 * mb + 8 * u + 4 * hl) = x;
+                    store_out4(out, row + 32 * mb + 8 * u + 4 * hl, x, BF16OUT);
                 }
             }
         }
@@ -698,12 +708,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
     const int nb_wg = (min(T, q0 + C::kBM) + 31) / 32; // key blocks the workgroup needs
     const int my_n = (qw < T) ? qw / 32 + 1 : 0;      // key blocks of this wave
 
-    const size_t q_stride = (size_t)Hq * D;
-    const size_t kv_stride = (size_t)Hkv * D;
-    const size_t qoff = ((size_t)b * T * Hq + h) * D;
-    const uint16_t* kbase = a.k + ((size_t)b * T * Hkv + g) * D;
-    const uint16_t* vbase = a.v + ((size_t)b * T * Hkv + g) * D;
-    const unsigned kv_row_bytes = (unsigned)kv_stride * 2u;
+    const uint16_t* kbase = a.k + (size_t)b * T * a.kv_rs + (size_t)g * D;
+    const uint16_t* vbase = a.v + (size_t)b * T * a.kv_rs + (size_t)g * D;
+    const unsigned kv_row_bytes = (unsigned)a.kv_rs * 2u;
 
     // DMA: wave w loads chunk w (rows 8w .. 8w+7 for D = 64) of K and of V of a block.
     // Blocks outside 0 .. nb_wg-1 reload the last block (into a stage nobody reads), so
@@ -741,10 +748,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
         for (int kd = 0; kd < C::kKD; ++kd) {
             u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u}, xo = {0u, 0u, 0u, 0u};
             if (row < T) {
-                const size_t off = qoff + (size_t)row * q_stride + 16 * kd + 8 * hl;
-                xq = load16(a.q + off);
-                xd = load16(a.dO + off);
-                xo = load16(a.o + off);
+                const size_t rowg = (size_t)b * T + row;
+                const int col = h * D + 16 * kd + 8 * hl;
+                xq = load16(a.q + rowg * a.q_rs + col);
+                xd = load16(a.dO + rowg * a.do_rs + col);
+                xo = load16(a.o + rowg * a.o_rs + col);
             }
             qreg[kd] = __builtin_bit_cast(bf16x8, xq);
             doreg[kd] = __builtin_bit_cast(bf16x8, xd);
@@ -886,7 +894,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
     if (query < T) {
         if (hl == 0) a.delta[((size_t)b * Hq + h) * T + query] = dfull;
         const float corr = dfull - dtilde;
-        float* drow = a.dq + qoff + (size_t)query * q_stride;
+        const size_t drow = ((size_t)b * T + query) * a.dq_rs + (size_t)h * D;
 #pragma unroll
         for (int mb = 0; mb < C::kMB; ++mb)
 #pragma unroll
@@ -894,7 +902,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
                 f32x4 x;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) x[r] = a.scale * fmaf(-corr, kbar[mb][4 * u + r], dqacc[mb][4 * u + r]);
-                *reinterpret_cast<f32x4*>(drow + 32 * mb + 8 * u + 4 * hl) = x;
+                store_out4(a.dq, drow + 32 * mb + 8 * u + 4 * hl, x, a.grad_bf16);
             }
     }
 }
@@ -928,8 +936,16 @@ static hipError_t launch_dkv_t(const BwdArgs& a, hipStream_t stream) {
     const long blocks = (long)x.n_tiles * a.B * a.Hkv;
     // One workgroup per CU fits (LDS and registers); gfx950 parts have 256 CUs.
     x.zigzag = blocks <= 256 ? 1 : 0;
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
-                       stream, x);
+    const dim3 grid((unsigned)blocks), block(C::kThreads);
+    const bool same = a.q_rs == a.do_rs;
+    if (same && !a.grad_bf16)
+        hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR, true, false>), grid, block, 0, stream, x);
+    else if (same)
+        hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR, true, true>), grid, block, 0, stream, x);
+    else if (!a.grad_bf16)
+        hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR, false, false>), grid, block, 0, stream, x);
+    else
+        hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR, false, true>), grid, block, 0, stream, x);
     return hipGetLastError();
 }
 

@@ -126,11 +126,11 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(FwdArgs 
     const int qw = q0 + C::kWQ * wave;   // first query of this wave
     const float c = a.scale_log2;
 
-    const size_t q_stride = (size_t)Hq * D;     // elements between consecutive t
-    const unsigned kv_row_bytes = (unsigned)(Hkv * D * 2);
-    const uint16_t* qbase = a.q + ((size_t)b * T * Hq + h) * D;
-    const char* kbase = reinterpret_cast<const char*>(a.k + ((size_t)b * T * Hkv + g) * D);
-    const char* vbase = reinterpret_cast<const char*>(a.v + ((size_t)b * T * Hkv + g) * D);
+    const size_t q_stride = (size_t)a.q_rs;     // elements between consecutive t
+    const unsigned kv_row_bytes = (unsigned)a.kv_rs * 2u;
+    const uint16_t* qbase = a.q + (size_t)b * T * a.q_rs + (size_t)h * D;
+    const char* kbase = reinterpret_cast<const char*>(a.k + (size_t)b * T * a.kv_rs + (size_t)g * D);
+    const char* vbase = reinterpret_cast<const char*>(a.v + (size_t)b * T * a.kv_rs + (size_t)g * D);
 
     // Keys needed: up to the last query of the workgroup, with T rounded up to whole
     // waves so that a wave's last block is always loaded (keys past T are masked for
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(FwdArgs 
         if (!active || query >= T) continue;
         const float l = sum_halves(lsum[qb]);
         const float inv = 1.0f / l;
-        uint16_t* orow = a.o + ((size_t)b * T + query) * q_stride + (size_t)h * D;
+        uint16_t* orow = a.o + ((size_t)b * T + query) * a.o_rs + (size_t)h * D;
 #pragma unroll
         for (int mb = 0; mb < C::kMB; ++mb) {
 #pragma unroll

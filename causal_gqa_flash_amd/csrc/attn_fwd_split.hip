@@ -512,8 +512,10 @@ __global__ __launch_bounds__(SplitCfg::kWaves * 64, 1) void attn_fwd_split_kerne
 
 // Shapes the balanced kernel handles: d = 64, whole 64-query blocks (at least two),
 // three query heads per kv head.
+// Contiguous tensors only (the kernel derives its row strides from the head counts).
 bool fwd_split_supported(const FwdArgs& a) {
-    return a.d == 64 && a.T % 64 == 0 && a.T >= 128 && a.Hq == SplitCfg::kG * a.Hkv;
+    return a.d == 64 && a.T % 64 == 0 && a.T >= 128 && a.Hq == SplitCfg::kG * a.Hkv &&
+           a.q_rs == a.Hq * a.d && a.kv_rs == a.Hkv * a.d && a.o_rs == a.Hq * a.d;
 }
 
 // Workgroups of the balanced kernel: one per (pair of query blocks, batch, kv head).

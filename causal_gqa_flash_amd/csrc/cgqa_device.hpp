@@ -278,6 +278,16 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Four consecutive outputs at element offset `off` of an output tensor that is fp32, or
+// bf16 (rounded to nearest even) when `bf16` is set.
+__device__ __forceinline__ void store_out4(void* base, size_t off, f32x4 x, bool bf16) {
+    if (bf16)
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + off) =
+            __builtin_bit_cast(u32x2, __builtin_convertvector(x, bf16x4));
+    else
+        *reinterpret_cast<f32x4*>(static_cast<float*>(base) + off) = x;
+}
+
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }

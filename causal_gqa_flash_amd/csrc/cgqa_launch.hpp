@@ -1,5 +1,9 @@
 // Host-side launch interface between the C-ABI entry points and the kernels.
 // Arguments arrive here already validated (shapes, alignment, d in {64, 128}).
+//
+// Tensor layout: element (b, t, h, c) of a [B, T, H, d] tensor with row stride rs (elements
+// between consecutive tokens, rs >= H*d) sits at (b*T + t)*rs + h*d + c; rs = H*d is the
+// contiguous layout. LSE and delta are always [B, Hq, T].
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -13,6 +17,7 @@ struct FwdArgs {
     uint16_t* o;
     float* lse;
     int B, T, Hq, Hkv, d;
+    int q_rs, kv_rs, o_rs;   // row strides of Q, of K and V, of O (elements)
     float scale_log2;   // scale * log2(e): scores in log2 units
     int n_qtiles;       // set by the launcher: query tiles per (batch, head)
     int n_pairs;        // set by the launcher: B * Hkv (batch, kv head) slices
@@ -27,10 +32,13 @@ struct BwdArgs {
     const uint16_t* dO;
     const float* lse;
     float* delta;       // written by the dq kernel, read by the dkv kernel
-    float* dq;
-    float* dk;
-    float* dv;
+    void* dq;           // fp32, or bf16 when grad_bf16
+    void* dk;
+    void* dv;
     int B, T, Hq, Hkv, d;
+    int q_rs, kv_rs, o_rs, do_rs;   // input row strides (elements)
+    int dq_rs, dkv_rs;              // output row strides (elements of the output type)
+    int grad_bf16;                  // 1: dQ, dK, dV rounded to bf16 (nearest even)
     float scale;        // softmax scale (dS carries it into dQ and dK)
     float scale_log2;   // scale * log2(e)
     int n_tiles;        // set by the launcher

@@ -16,11 +16,13 @@
  *   k, v     : [B][T][Hkv][d]  bfloat16
  *   lse      : [B][Hq][T]      float32, natural-log log-sum-exp of each row of
  *                              scale * q.k over keys 0..i (causal, inclusive)
- *   delta    : [B][Hq][T]      float32, D_i = sum_c dO[i,c] * O[i,c]
+ *   delta    : [B][Hq][T]      float32, D_i = sum_j P_ij dP_ij (= sum_c dO[i,c] * O[i,c]
+ *                              in exact arithmetic)
  *   dq       : [B][T][Hq][d]   float32
  *   dk, dv   : [B][T][Hkv][d]  float32
  * Query head h uses key/value head h / (Hq / Hkv). Query i sees keys 0..i.
  * d must be 64 or 128. Every pointer must be 16-byte aligned device memory.
+ * The *_strided calls below take the same tensors with a row stride each (see there).
  *
  * Every call only enqueues work on `stream` (a hipStream_t; NULL = the default
  * stream) and returns; outputs are valid once the caller synchronises with the stream.
@@ -45,10 +47,13 @@ extern "C" {
 enum {
     CGQA_OK = 0,
     /* null pointer with non-empty sizes, negative size, Hq or Hkv < 1, Hq % Hkv != 0,
-       scale not finite or not positive, an element count of 2^31 or more,
-       or an output that overlaps another buffer */
+       scale not finite or not positive, an element count of 2^31 or more, a row stride
+       shorter than its row, an unknown gradient type, or an output that overlaps
+       another buffer */
     CGQA_EINVAL = 1,
-    /* head dimension other than 64 or 128, or a pointer not 16-byte aligned */
+    /* head dimension other than 64 or 128, a pointer not 16-byte aligned, or a row
+       stride that is not a whole number of 16-byte units (inputs) or 8-byte units
+       (outputs) */
     CGQA_EUNSUPPORTED = 2,
     /* the kernel launch was refused by the HIP runtime (cgqa_last_hip_error() tells
        which HIP error, for the calling thread) */
@@ -63,9 +68,10 @@ int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
              int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
 
 /* Backward, query side (section "The same bits every time": each block of queries
- * has a single owning workgroup). For the loss L = sum(O * dO): recomputes P from q, k and lse, writes
- * delta = rowsum(dO * o) (from the bf16 o given) and dq = dL/dq.
- * Reads q, k, v, o, dO, lse; overwrites delta and dq. */
+ * has a single owning workgroup). For the loss L = sum(O * dO): recomputes P from q, k
+ * and lse, writes delta = D_i = sum_j P_ij dP_ij (accumulated in fp32 inside the kernel;
+ * it equals rowsum(dO * O), which the bf16 o would give only to bf16 accuracy) and
+ * dq = dL/dq. Reads q, k, v, o, dO, lse; overwrites delta and dq. */
 int attn_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 const uint16_t* o, const uint16_t* dO, const float* lse,
                 float* delta, float* dq,
@@ -81,6 +87,50 @@ int attn_bwd_dkv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                  const uint16_t* dO, const float* lse, const float* delta,
                  float* dk, float* dv,
                  int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
+
+/* Strided variants: the same operations on tensors that sit inside wider rows, e.g. the
+ * packed [B*T][(Hq + 2*Hkv)*d] buffer that one fused projection produces for queries,
+ * keys and values (page "A transformer in PTX", section "The model": one fused matmul
+ * computes them) with q = base, k = base + Hq*d, v = base + (Hq + Hkv)*d, and gradients
+ * written into a packed buffer of the same shape.
+ *
+ * Element (b, t, h, c) of a tensor with row stride rs is at (b*T + t)*rs + h*d + c, in
+ * elements of the tensor's own type; rs = H*d is the contiguous layout of the calls
+ * above, which these reproduce bit for bit. Each stride must be at least its row (H*d)
+ * and at most such that B*T*rs < 2^31. The strides of bf16 tensors a call reads (q, k
+ * and v; o and dO in the backward) must be multiples of 8 elements, those of the outputs
+ * (o in the forward; dq, dk and dv) multiples of 4 elements.
+ * k and v share kv_row_stride; dk and dv share dkv_row_stride.
+ *
+ * grad_dtype selects the type of dq, dk and dv: CGQA_GRAD_F32 (float) or CGQA_GRAD_BF16
+ * (bfloat16 bit patterns, rounded to nearest even from the same float values the float
+ * outputs hold). lse and delta stay [B][Hq][T] float32.
+ *
+ * Outputs may share a buffer with each other when their row strides (in bytes) are
+ * equal and their column ranges within a row do not meet (dq, dk, dv of one packed
+ * buffer); any other overlap of an output with another tensor is CGQA_EINVAL. */
+enum { CGQA_GRAD_F32 = 0, CGQA_GRAD_BF16 = 1 };
+
+int attn_fwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     uint16_t* o, float* lse,
+                     int B, int T, int Hq, int Hkv, int d,
+                     int q_row_stride, int kv_row_stride, int o_row_stride,
+                     float scale, void* stream);
+
+int attn_bwd_dq_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const uint16_t* o, const uint16_t* dO, const float* lse,
+                        float* delta, void* dq,
+                        int B, int T, int Hq, int Hkv, int d,
+                        int q_row_stride, int kv_row_stride, int o_row_stride,
+                        int do_row_stride, int dq_row_stride, int grad_dtype,
+                        float scale, void* stream);
+
+int attn_bwd_dkv_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dO, const float* lse, const float* delta,
+                         void* dk, void* dv,
+                         int B, int T, int Hq, int Hkv, int d,
+                         int q_row_stride, int kv_row_stride, int do_row_stride,
+                         int dkv_row_stride, int grad_dtype, float scale, void* stream);
 
 /* Static description of a return code (never NULL). */
 const char* attn_status_string(int status);

@@ -130,3 +130,104 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "HERE", str(tmp_path))
     with pytest.raises(ImportError):
         _binding.library()
+
+
+# ---- strided entry points (every call below is rejected before any HIP call)
+
+def strides(a, **kw):
+    Hq, Hkv, d = a["Hq"], a["Hkv"], a["d"]
+    s = dict(q_rs=Hq * d, kv_rs=Hkv * d, o_rs=Hq * d, do_rs=Hq * d, dq_rs=Hq * d, dkv_rs=Hkv * d, grad=0)
+    s.update(kw)
+    return s
+
+
+def call_fwd_s(ptrs=None, st=None, **kw):
+    a = dict(GOOD, **kw)
+    s = strides(a, **(st or {}))
+    p = ptrs or [fake(i) for i in range(5)]
+    return cg.library().attn_fwd_strided(*p, a["B"], a["T"], a["Hq"], a["Hkv"], a["d"],
+                                         s["q_rs"], s["kv_rs"], s["o_rs"], a["scale"], None)
+
+
+def call_dq_s(ptrs=None, st=None, **kw):
+    a = dict(GOOD, **kw)
+    s = strides(a, **(st or {}))
+    p = ptrs or [fake(i) for i in range(8)]
+    return cg.library().attn_bwd_dq_strided(*p, a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], s["q_rs"],
+                                            s["kv_rs"], s["o_rs"], s["do_rs"], s["dq_rs"], s["grad"],
+                                            a["scale"], None)
+
+
+def call_dkv_s(ptrs=None, st=None, **kw):
+    a = dict(GOOD, **kw)
+    s = strides(a, **(st or {}))
+    p = ptrs or [fake(i) for i in range(8)]
+    return cg.library().attn_bwd_dkv_strided(*p, a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], s["q_rs"],
+                                             s["kv_rs"], s["do_rs"], s["dkv_rs"], s["grad"], a["scale"], None)
+
+
+STRIDED = [(call_fwd_s, 5, (3, 4)), (call_dq_s, 8, (6, 7)), (call_dkv_s, 8, (6, 7))]
+
+
+@pytest.mark.parametrize("call", [c for c, _, _ in STRIDED])
+@pytest.mark.parametrize("kw,code", BAD_SHAPES)
+def test_strided_bad_shapes_rejected(call, kw, code):
+    assert call(**kw) == code
+
+
+@pytest.mark.parametrize("call,n,outs", STRIDED)
+def test_strided_null_misaligned_overlapping_rejected(call, n, outs):
+    for i in range(n):
+        p = [fake(j) for j in range(n)]
+        p[i] = None
+        assert call(ptrs=p) == cg.CGQA_EINVAL, i
+        p = [fake(j) for j in range(n)]
+        p[i] += 8
+        assert call(ptrs=p) == cg.CGQA_EUNSUPPORTED, i
+    for o in outs:
+        for other in range(n):
+            if other != o:
+                p = [fake(j) for j in range(n)]
+                p[o] = p[other] + 64
+                assert call(ptrs=p) == cg.CGQA_EINVAL, (o, other)
+
+
+# (call, stride name, row width in elements (Hq*d = 384, Hkv*d = 128), alignment)
+STRIDE_ARGS = [(call_fwd_s, "q_rs", 384, 8), (call_fwd_s, "kv_rs", 128, 8), (call_fwd_s, "o_rs", 384, 4),
+               (call_dq_s, "q_rs", 384, 8), (call_dq_s, "kv_rs", 128, 8), (call_dq_s, "o_rs", 384, 8),
+               (call_dq_s, "do_rs", 384, 8), (call_dq_s, "dq_rs", 384, 4),
+               (call_dkv_s, "q_rs", 384, 8), (call_dkv_s, "kv_rs", 128, 8), (call_dkv_s, "do_rs", 384, 8),
+               (call_dkv_s, "dkv_rs", 128, 4)]
+
+
+@pytest.mark.parametrize("call,name,width,align", STRIDE_ARGS)
+def test_bad_strides_rejected(call, name, width, align):
+    assert call(st={name: width - 8}) == cg.CGQA_EINVAL           # shorter than its row
+    assert call(st={name: -width}) == cg.CGQA_EINVAL
+    assert call(st={name: width + align // 2}) == cg.CGQA_EUNSUPPORTED   # not whole units
+    # B*T*rs reaches 2^31 elements
+    assert call(st={name: 1 << 15}, B=1, T=1 << 16) == cg.CGQA_EINVAL
+    # the empty problem still checks its strides
+    assert call(st={name: width - 8}, T=0) == cg.CGQA_EINVAL
+
+
+@pytest.mark.parametrize("call", [call_dq_s, call_dkv_s])
+def test_unknown_gradient_type_rejected(call):
+    for g in (-1, 2, 7):
+        assert call(st={"grad": g}) == cg.CGQA_EINVAL
+
+
+def test_packed_gradients_must_not_share_columns():
+    # dk and dv in one buffer with row stride R = (Hq + 2 Hkv) d = 640 floats: dv placed
+    # 64 bytes after dk lies inside dk's 128 columns of every row.
+    R = 640
+    p = [fake(j) for j in range(8)]
+    p[7] = p[6] + 64
+    assert call_dkv_s(ptrs=p, st={"dkv_rs": R}) == cg.CGQA_EINVAL
+    # bf16 dv one row-window too far: its columns [96, 224) meet dk's [0, 128)
+    p[7] = p[6] + 2 * 96
+    assert call_dkv_s(ptrs=p, st={"dkv_rs": R, "grad": 1}) == cg.CGQA_EINVAL
+    # dq written into the input q buffer's rows (q's columns) is an overlap
+    p = [fake(j) for j in range(8)]
+    p[7] = p[0] + 16
+    assert call_dq_s(ptrs=p, st={"q_rs": 640, "dq_rs": 320}) == cg.CGQA_EINVAL
