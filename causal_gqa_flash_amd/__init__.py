@@ -17,6 +17,9 @@ from ._binding import (  # noqa: F401
     attn_bwd_dkv,
     attn_bwd_dq,
     attn_fwd,
+    attn_naive_bwd,
+    attn_naive_fwd,
+    attn_naive_workspace_bytes,
     attn_status_string,
     library,
     library_path,

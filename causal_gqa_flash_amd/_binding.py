@@ -51,6 +51,13 @@ def library():
         lib.attn_bwd_dq_strided.restype = i
         lib.attn_bwd_dkv_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, vp]
         lib.attn_bwd_dkv_strided.restype = i
+        sz = ctypes.c_size_t
+        lib.attn_naive_workspace_bytes.argtypes = [i, i, i]
+        lib.attn_naive_workspace_bytes.restype = sz
+        lib.attn_naive_fwd.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+        lib.attn_naive_fwd.restype = i
+        lib.attn_naive_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+        lib.attn_naive_bwd.restype = i
         lib.attn_status_string.argtypes = [i]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.cgqa_last_hip_error.argtypes = []
@@ -218,3 +225,65 @@ def attn_bwd_dkv(q, k, v, do, lse, delta, scale=None, dk=None, dv=None, stream=N
             _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
             B, T, Hq, Hkv, d, rq, rkv, rdo, rdk, _grad_code(dk.dtype), _scale(scale, d), _stream_ptr(stream)))
     return dk, dv
+
+
+def attn_naive_workspace_bytes(B, T, Hq):
+    return int(library().attn_naive_workspace_bytes(int(B), int(T), int(Hq)))
+
+
+def _workspace(B, T, Hq, workspace, device):
+    torch = _torch()
+    need = attn_naive_workspace_bytes(B, T, Hq)
+    if workspace is None:
+        workspace = torch.empty((max(need, 4) // 4,), dtype=torch.float32, device=device)
+    if workspace.dtype != torch.float32 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous float32 device tensor")
+    return workspace
+
+
+def attn_naive_fwd(q, k, v, scale=None, o=None, lse=None, workspace=None, stream=None):
+    """Naive attention (the GPU reference mode): o [B,T,Hq,d] bf16 and lse [B,Hq,T] fp32
+    with every T x T probability stored in `workspace` (fp32, allocated if None).
+    Contiguous tensors; 1 <= d <= 128."""
+    torch = _torch()
+    B, T, Hq, Hkv, d = _dims(q, k)
+    _need(q, "q", torch.bfloat16, (B, T, Hq, d))
+    _need(k, "k", torch.bfloat16, (B, T, Hkv, d))
+    _need(v, "v", torch.bfloat16, (B, T, Hkv, d))
+    if o is None:
+        o = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.bfloat16, (B, T, Hq, d))
+    _need(lse, "lse", torch.float32, (B, Hq, T))
+    ws = _workspace(B, T, Hq, workspace, q.device)
+    _check("attn_naive_fwd", library().attn_naive_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * 4,
+        B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
+    return o, lse
+
+
+def attn_naive_bwd(q, k, v, do, scale=None, delta=None, dq=None, dk=None, dv=None, workspace=None,
+                   stream=None):
+    """Naive backward of L = sum(O * dO): delta [B,Hq,T], dq [B,T,Hq,d], dk, dv [B,T,Hkv,d],
+    all fp32, recomputing the probabilities into `workspace`. Contiguous tensors."""
+    torch = _torch()
+    B, T, Hq, Hkv, d = _dims(q, k)
+    _need(q, "q", torch.bfloat16, (B, T, Hq, d))
+    _need(k, "k", torch.bfloat16, (B, T, Hkv, d))
+    _need(v, "v", torch.bfloat16, (B, T, Hkv, d))
+    _need(do, "do", torch.bfloat16, (B, T, Hq, d))
+    f32 = dict(dtype=torch.float32, device=q.device)
+    delta = torch.empty((B, Hq, T), **f32) if delta is None else delta
+    dq = torch.empty((B, T, Hq, d), **f32) if dq is None else dq
+    dk = torch.empty((B, T, Hkv, d), **f32) if dk is None else dk
+    dv = torch.empty((B, T, Hkv, d), **f32) if dv is None else dv
+    _need(delta, "delta", torch.float32, (B, Hq, T))
+    _need(dq, "dq", torch.float32, (B, T, Hq, d))
+    _need(dk, "dk", torch.float32, (B, T, Hkv, d))
+    _need(dv, "dv", torch.float32, (B, T, Hkv, d))
+    ws = _workspace(B, T, Hq, workspace, q.device)
+    _check("attn_naive_bwd", library().attn_naive_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+        ws.numel() * 4, B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
+    return delta, dq, dk, dv

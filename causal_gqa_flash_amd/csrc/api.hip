@@ -38,12 +38,13 @@ bool disjoint(View a, View b) {
 }
 
 // Shape checks shared by the calls. Returns CGQA_OK, or sets *empty for B or T = 0.
-int check_shape(int B, int T, int Hq, int Hkv, int d, float scale, bool* empty) {
+// The flash kernels take d = 64 or 128, the naive ones any d from 1 to 128.
+int check_shape(int B, int T, int Hq, int Hkv, int d, float scale, bool* empty, bool naive = false) {
     *empty = false;
     if (B < 0 || T < 0 || Hq < 1 || Hkv < 1) return CGQA_EINVAL;
     if (Hq % Hkv != 0) return CGQA_EINVAL;
     if (!(scale > 0.0f) || !isfinite(scale)) return CGQA_EINVAL;
-    if (d != 64 && d != 128) return CGQA_EUNSUPPORTED;
+    if (naive ? (d < 1 || d > 128) : (d != 64 && d != 128)) return CGQA_EUNSUPPORTED;
     if ((int64_t)B * Hq * T >= ((int64_t)1 << 31)) return CGQA_EINVAL;
     if (B == 0 || T == 0) *empty = true;
     return CGQA_OK;
@@ -157,9 +158,83 @@ int bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
                         : cgqa::launch_bwd_dkv(a, (hipStream_t)stream));
 }
 
+// Bytes of the naive workspace, or -1 for sizes no call accepts.
+int64_t naive_ws_bytes(int B, int T, int Hq) {
+    if (B < 0 || T < 0 || Hq < 1 || (int64_t)B * Hq * T >= ((int64_t)1 << 31)) return -1;
+    return (int64_t)B * Hq * T * T * 4;
+}
+
+// Both naive calls: contiguous tensors, an fp32 workspace of B*Hq*T*T floats that
+// overlaps nothing else. Inputs in[0..nin), outputs out[0..nout) as byte views.
+int naive_impl(bool fwd, const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
+               uint16_t* o, float* lse, float* delta, float* dq, float* dk, float* dv, float* ws,
+               size_t ws_bytes, int B, int T, int Hq, int Hkv, int d, float scale, void* stream) {
+    bool empty = false;
+    int rc = check_shape(B, T, Hq, Hkv, d, scale, &empty, true);
+    if (rc != CGQA_OK) return rc;
+    const int64_t rows = (int64_t)B * T, wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d, nr = (int64_t)B * Hq * T;
+    if (rows * wq >= ((int64_t)1 << 31)) return CGQA_EINVAL;
+    if (empty) return CGQA_OK;
+    const int64_t need = naive_ws_bytes(B, T, Hq);
+    if (!ws || (uint64_t)ws_bytes < (uint64_t)need) return CGQA_EINVAL;
+    const View vq{q, rows, wq, wq, 2}, vk{k, rows, wkv, wkv, 2}, vv{v, rows, wkv, wkv, 2},
+        vw{ws, 1, need / 4, need / 4, 4};
+    if (fwd) {
+        if (!q || !k || !v || !o || !lse) return CGQA_EINVAL;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(ws))
+            return CGQA_EUNSUPPORTED;
+        const View outs[3] = {View{o, rows, wq, wq, 2}, View{lse, 1, nr, nr, 4}, vw};
+        const View ins[3] = {vq, vk, vv};
+        for (int x = 0; x < 3; ++x) {
+            for (int y = x + 1; y < 3; ++y)
+                if (!disjoint(outs[x], outs[y])) return CGQA_EINVAL;
+            for (const View& s : ins)
+                if (!disjoint(s, outs[x])) return CGQA_EINVAL;
+        }
+    } else {
+        if (!q || !k || !v || !dO || !delta || !dq || !dk || !dv) return CGQA_EINVAL;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(delta) ||
+            !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(ws))
+            return CGQA_EUNSUPPORTED;
+        const View outs[5] = {View{delta, 1, nr, nr, 4}, View{dq, rows, wq, wq, 4}, View{dk, rows, wkv, wkv, 4},
+                              View{dv, rows, wkv, wkv, 4}, vw};
+        const View ins[4] = {vq, vk, vv, View{dO, rows, wq, wq, 2}};
+        for (int x = 0; x < 5; ++x) {
+            for (int y = x + 1; y < 5; ++y)
+                if (!disjoint(outs[x], outs[y])) return CGQA_EINVAL;
+            for (const View& s : ins)
+                if (!disjoint(s, outs[x])) return CGQA_EINVAL;
+        }
+    }
+    cgqa::NaiveArgs a{};
+    a.q = q; a.k = k; a.v = v; a.dO = dO; a.o = o; a.lse = lse; a.delta = delta;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.p = ws;
+    a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.scale = scale;
+    return finish(fwd ? cgqa::launch_naive_fwd(a, (hipStream_t)stream) : cgqa::launch_naive_bwd(a, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t attn_naive_workspace_bytes(int B, int T, int Hq) {
+    const int64_t n = naive_ws_bytes(B, T, Hq);
+    return n < 0 ? 0 : (size_t)n;
+}
+
+int attn_naive_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                   float* workspace, size_t workspace_bytes, int B, int T, int Hq, int Hkv, int d,
+                   float scale, void* stream) {
+    return naive_impl(true, q, k, v, nullptr, o, lse, nullptr, nullptr, nullptr, nullptr, workspace,
+                      workspace_bytes, B, T, Hq, Hkv, d, scale, stream);
+}
+
+int attn_naive_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
+                   float* delta, float* dq, float* dk, float* dv, float* workspace, size_t workspace_bytes,
+                   int B, int T, int Hq, int Hkv, int d, float scale, void* stream) {
+    return naive_impl(false, q, k, v, dO, nullptr, nullptr, delta, dq, dk, dv, workspace, workspace_bytes,
+                      B, T, Hq, Hkv, d, scale, stream);
+}
 
 int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
              int B, int T, int Hq, int Hkv, int d, float scale, void* stream) {

@@ -45,6 +45,24 @@ struct BwdArgs {
     int zigzag;         // dK/dV: deal key blocks in zig-zag order (set by the launcher)
 };
 
+// Naive attention (attn_naive.hip): contiguous tensors, fp32 workspace p of B*Hq*T*T
+// floats, 1 <= d <= 128.
+struct NaiveArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* dO;   // backward only
+    uint16_t* o;          // forward only
+    float* lse;           // forward only (null in the backward, which recomputes P)
+    float* delta;         // backward only
+    float* dq;
+    float* dk;
+    float* dv;
+    float* p;             // workspace
+    int B, T, Hq, Hkv, d;
+    float scale;
+};
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // Balanced forward for d = 64 and whole 64-query blocks (attn_fwd_split.hip).
 bool fwd_split_supported(const FwdArgs& a);
@@ -52,5 +70,7 @@ long fwd_split_blocks(const FwdArgs& a);
 hipError_t launch_fwd_split(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkv(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_naive_fwd(const NaiveArgs& a, hipStream_t stream);
+hipError_t launch_naive_bwd(const NaiveArgs& a, hipStream_t stream);
 
 }  // namespace cgqa

@@ -38,6 +38,7 @@
 #ifndef CGQA_H
 #define CGQA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -131,6 +132,34 @@ int attn_bwd_dkv_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          int B, int T, int Hq, int Hkv, int d,
                          int q_row_stride, int kv_row_stride, int do_row_stride,
                          int dkv_row_stride, int grad_dtype, float scale, void* stream);
+
+/* Naive attention, the GPU reference mode (page "A transformer in PTX", section "Three
+ * ways to run it": the fast kernels are checked against naive ones; section "Flash
+ * attention": naive kernels store the whole T x T score matrix of every head). Same
+ * operation, shapes and layouts as attn_fwd / attn_bwd_dq + attn_bwd_dkv for contiguous
+ * tensors, computed step by step in fp32: scores into `workspace`, a row softmax in place,
+ * then the products, each sum in a fixed order (repeatable bits). d may be any value from
+ * 1 to 128 (CGQA_EUNSUPPORTED otherwise).
+ *
+ * workspace: caller-owned device memory of at least attn_naive_workspace_bytes(B, T, Hq)
+ * bytes (fp32 [B][Hq][T][T]; only entries with key <= query are used), 16-byte aligned,
+ * overlapping no other argument; its contents on return are unspecified. A missing or
+ * smaller workspace is CGQA_EINVAL. Calls that share a workspace must be ordered on the
+ * GPU (one stream, or events).
+ *
+ * attn_naive_fwd writes o (bf16, rounded to nearest even from fp32) and lse.
+ * attn_naive_bwd recomputes the probabilities itself (it reads no o or lse) and writes
+ * delta = D_i = sum_j P_ij dP_ij and the fp32 gradients dq, dk, dv of L = sum(O * dO). */
+size_t attn_naive_workspace_bytes(int B, int T, int Hq);   /* 0 for sizes no call accepts */
+
+int attn_naive_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                   uint16_t* o, float* lse, float* workspace, size_t workspace_bytes,
+                   int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
+
+int attn_naive_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
+                   float* delta, float* dq, float* dk, float* dv,
+                   float* workspace, size_t workspace_bytes,
+                   int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
 
 /* Static description of a return code (never NULL). */
 const char* attn_status_string(int status);

@@ -231,3 +231,88 @@ def test_packed_gradients_must_not_share_columns():
     p = [fake(j) for j in range(8)]
     p[7] = p[0] + 16
     assert call_dq_s(ptrs=p, st={"q_rs": 640, "dq_rs": 320}) == cg.CGQA_EINVAL
+
+
+# ---- naive attention (the GPU reference mode). Every call below is rejected too.
+def naive_need(a):
+    return a["B"] * a["Hq"] * a["T"] * a["T"] * 4
+
+
+def call_nfwd(ptrs=None, ws_bytes=None, **kw):
+    a = dict(GOOD, **kw)
+    p = ptrs or [fake(i) for i in range(6)]
+    n = naive_need(a) if ws_bytes is None else ws_bytes
+    return cg.library().attn_naive_fwd(*p[:5], p[5], n, a["B"], a["T"], a["Hq"], a["Hkv"], a["d"],
+                                       a["scale"], None)
+
+
+def call_nbwd(ptrs=None, ws_bytes=None, **kw):
+    a = dict(GOOD, **kw)
+    p = ptrs or [fake(i) for i in range(9)]
+    n = naive_need(a) if ws_bytes is None else ws_bytes
+    return cg.library().attn_naive_bwd(*p[:8], p[8], n, a["B"], a["T"], a["Hq"], a["Hkv"], a["d"],
+                                       a["scale"], None)
+
+
+NAIVE_BAD_SHAPES = [s for s in BAD_SHAPES if "d" not in s[0]] + [
+    (dict(d=0), cg.CGQA_EUNSUPPORTED),
+    (dict(d=129), cg.CGQA_EUNSUPPORTED),
+    (dict(d=256), cg.CGQA_EUNSUPPORTED),
+]
+
+
+def test_naive_workspace_bytes():
+    assert cg.attn_naive_workspace_bytes(16, 1024, 6) == 16 * 6 * 1024 * 1024 * 4
+    assert cg.attn_naive_workspace_bytes(0, 64, 6) == 0
+    assert cg.attn_naive_workspace_bytes(-1, 64, 6) == 0
+    assert cg.attn_naive_workspace_bytes(1, 64, 0) == 0
+    assert cg.attn_naive_workspace_bytes(1 << 16, 1 << 12, 8) == 0   # 2^31 rows
+    assert cg.attn_naive_workspace_bytes(1 << 14, 1 << 12, 8) == (1 << 29) * (1 << 12) * 4
+
+
+@pytest.mark.parametrize("call", [call_nfwd, call_nbwd])
+@pytest.mark.parametrize("kw,code", NAIVE_BAD_SHAPES)
+def test_naive_bad_shapes_rejected(call, kw, code):
+    a = dict(GOOD, **kw)
+    ws = max(0, naive_need(a)) if a["B"] >= 0 and a["T"] >= 0 and a["Hq"] >= 1 else 0
+    assert call(ws_bytes=ws, **kw) == code
+
+
+@pytest.mark.parametrize("call", [call_nfwd, call_nbwd])
+def test_naive_small_or_missing_workspace_rejected(call):
+    need = naive_need(GOOD)
+    assert call(ws_bytes=need - 1) == cg.CGQA_EINVAL
+    assert call(ws_bytes=0) == cg.CGQA_EINVAL
+    n = 6 if call is call_nfwd else 9
+    p = [fake(j) for j in range(n)]
+    p[-1] = None
+    assert call(ptrs=p) == cg.CGQA_EINVAL
+
+
+@pytest.mark.parametrize("call,n", [(call_nfwd, 6), (call_nbwd, 9)])
+def test_naive_null_and_misaligned_rejected(call, n):
+    for i in range(n):
+        p = [fake(j) for j in range(n)]
+        p[i] = None
+        assert call(ptrs=p) == cg.CGQA_EINVAL, i
+        p = [fake(j) for j in range(n)]
+        p[i] += 4
+        assert call(ptrs=p) == cg.CGQA_EUNSUPPORTED, i
+
+
+@pytest.mark.parametrize("call,n,outs", [(call_nfwd, 6, (3, 4, 5)), (call_nbwd, 9, (4, 5, 6, 7, 8))])
+def test_naive_overlaps_rejected(call, n, outs):
+    for o in outs:
+        for other in range(n):
+            if other == o:
+                continue
+            p = [fake(j) for j in range(n)]
+            p[o] = p[other] + 64
+            assert call(ptrs=p) == cg.CGQA_EINVAL, (o, other)
+
+
+@pytest.mark.parametrize("call", [call_nfwd, call_nbwd])
+def test_naive_empty_problem_is_a_no_op(call):
+    n = 6 if call is call_nfwd else 9
+    assert call(ptrs=[None] * n, ws_bytes=0, T=0) == cg.CGQA_OK
+    assert call(ptrs=[None] * n, ws_bytes=0, B=0) == cg.CGQA_OK

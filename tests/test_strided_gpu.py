@@ -97,10 +97,10 @@ def test_packed_qkv_matches_contiguous(B, T, Hq, Hkv, d, seed):
 
 
 # Tolerance of bf16 gradients against the oracle: the fp32 value g is within MAX_ABS of the
-# exact r (and within REL_L2 in relative L2); rounding g to bf16 moves it by at most 2^-9 |g|
-# (half a unit in the last of 8 significant bits), so |bf16(g) - r| <= MAX_ABS + 2^-9 (|r| +
-# MAX_ABS) element-wise and the relative L2 error grows by at most 2^-9 (1 + REL_L2).
-BF16_HALF_ULP = 2.0 ** -9
+# exact r (and within REL_L2 in relative L2); rounding g to bf16 moves it by at most u |g|,
+# u = 2^-8 the unit roundoff of 8 significant bits, so |bf16(g) - r| <= MAX_ABS + u (|r| +
+# MAX_ABS) element-wise and the relative L2 error grows by at most u (1 + REL_L2).
+BF16_UNIT_ROUNDOFF = 2.0 ** -8
 
 
 @pytest.mark.parametrize("B,T,Hq,Hkv,d,seed", SHAPES[::2])
@@ -121,7 +121,7 @@ def test_bf16_gradients_against_oracle(B, T, Hq, Hkv, d, seed):
         got = t.float().cpu().numpy().astype(np.float64)
         r = want[name]
         err = np.abs(got - r)
-        bound = MAX_ABS + BF16_HALF_ULP * (np.abs(r) + MAX_ABS)
+        bound = MAX_ABS + BF16_UNIT_ROUNDOFF * (np.abs(r) + MAX_ABS)
         assert np.all(err <= bound), (name, tuple(np.argwhere(err > bound)[0]), float(err.max()))
         rel = np.linalg.norm(got - r) / np.linalg.norm(r)
-        assert rel <= REL_L2 + BF16_HALF_ULP * (1 + REL_L2), (name, rel)
+        assert rel <= REL_L2 + BF16_UNIT_ROUNDOFF * (1 + REL_L2), (name, rel)
