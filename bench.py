@@ -159,6 +159,7 @@ def main():
                          "leave their idle state (the first tens of ms run 5-11%% slower)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-naive", action="store_true", help="skip timing the naive reference mode")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="run the short workload that rocprofv3 --pmc profiles (see profiles/)")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -285,6 +286,23 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": None,
     }
+    if not args.no_naive:
+        # The naive reference mode on the same inputs (outside the timed step): every
+        # T x T probability goes through an fp32 workspace in HBM.
+        ws = torch.empty((cg.attn_naive_workspace_bytes(w.B, w.T, w.Hq) // 4,), dtype=torch.float32,
+                         device="cuda")
+        def naive_fwd():
+            cg.attn_naive_fwd(q, k, v, scale=w.scale, workspace=ws, stream=stream)
+        def naive_bwd():
+            cg.attn_naive_bwd(q, k, v, do, scale=w.scale, workspace=ws, stream=stream)
+        naive_fwd(); naive_bwd()
+        torch.cuda.synchronize()
+        nf, nb = timed(naive_fwd, 3), timed(naive_bwd, 3)
+        out["naive"] = {"fwd_ms": round(nf, 4), "bwd_ms": round(nb, 4),
+                        "workspace_bytes": int(ws.numel() * 4),
+                        "flash_speedup_fwd": round(nf / ms_k["attn_fwd"], 1),
+                        "flash_speedup_bwd": round(nb / bwd_ms, 1)}
+        del ws
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
