@@ -123,6 +123,50 @@ def pmc_summarize(fetch_dir, write_dir, out_path):
     print(json.dumps(out), flush=True)
 
 
+def gemm_bench(w, timed, stream):
+    """The projections around attention for the workload's B*T tokens (model width Hq*d,
+    fused QKV width (Hq + 2 Hkv) d): forward QKV and WO (+ residual), and the QKV
+    projection's dX and dW, each timed through cgqa_gemm, with torch.matmul (hipBLASLt)
+    on the same bf16 operands beside it for reference."""
+    import torch
+    import causal_gqa_flash_amd as cg
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    Mt, D, Q = w.B * w.T, w.Hq * w.d, (w.Hq + 2 * w.Hkv) * w.d
+    rnd = lambda *s: (torch.randn(*s, generator=g, device="cuda") * 0.05).to(torch.bfloat16)
+    x, wqkv, wo, dqkv = rnd(Mt, D), rnd(Q, D), rnd(D, D), rnd(Mt, Q)
+    resid = torch.randn(Mt, D, generator=g, device="cuda")
+    c_qkv = torch.empty(Mt, Q, dtype=torch.bfloat16, device="cuda")
+    c_f32 = torch.empty(Mt, D, device="cuda")
+    c_dw = torch.empty(Q, D, device="cuda")
+    ws_dw = torch.empty((max(cg.gemm_workspace_bytes(Q, D, Mt), 4) // 4,), device="cuda")
+    cases = {
+        "qkv": (Mt, Q, D, lambda: cg.gemm(x, wqkv, c=c_qkv, stream=stream),
+                lambda: torch.matmul(x, wqkv.t())),
+        "wo_residual": (Mt, D, D, lambda: cg.gemm(x, wo, r=resid, c=c_f32, stream=stream),
+                        lambda: torch.matmul(x, wo.t())),
+        "dx_qkv": (Mt, D, Q, lambda: cg.gemm(dqkv, wqkv, c=c_f32, b_kn=True, stream=stream),
+                   lambda: torch.matmul(dqkv, wqkv)),
+        "dw_qkv": (Q, D, Mt, lambda: cg.gemm(dqkv, x, c=c_dw, a_km=True, b_kn=True, workspace=ws_dw,
+                                             stream=stream),
+                   lambda: torch.matmul(dqkv.t(), x)),
+    }
+    res, best = {}, None
+    for name, (M, N, K, ours, lib) in cases.items():
+        ours(); lib()
+        torch.cuda.synchronize()
+        ms, ms_lib = timed(ours, 20), timed(lib, 20)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        res[name] = {"M": M, "N": N, "K": K, "ms": round(ms, 5), "tflops": round(tf, 1),
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "torch_matmul_ms": round(ms_lib, 5)}
+        if best is None or tf > best[1]:
+            best = (name, tf)
+    return {"shapes": res, "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (" + best[0] + ")",
+                                        "achieved": round(best[1], 1), "peak": PEAK_BF16_TFLOPS,
+                                        "unit": "TFLOP/s", "frac": round(best[1] / PEAK_BF16_TFLOPS, 4)},
+            "note": "torch_matmul_ms: torch.matmul on the same bf16 operands (bf16 output)"}
+
+
 def cpu_baseline(w, x, budget_s):
     """The fp64 CPU oracle (as it is) on whole (batch, kv head) slices of the workload,
     forward and backward, until about budget_s seconds have passed."""
@@ -160,6 +204,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-naive", action="store_true", help="skip timing the naive reference mode")
+    ap.add_argument("--no-gemm", action="store_true", help="skip timing the projection matmuls")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="run the short workload that rocprofv3 --pmc profiles (see profiles/)")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -303,6 +348,8 @@ def main():
                         "flash_speedup_fwd": round(nf / ms_k["attn_fwd"], 1),
                         "flash_speedup_bwd": round(nb / bwd_ms, 1)}
         del ws
+    if not args.no_gemm:
+        out["gemm"] = gemm_bench(w, timed, stream)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -10,6 +10,9 @@ from ._binding import (  # noqa: F401
     CGQA_EHIP,
     CGQA_EINVAL,
     CGQA_EUNSUPPORTED,
+    CGQA_GEMM_A_KM,
+    CGQA_GEMM_B_KN,
+    CGQA_GEMM_C_BF16,
     CGQA_GRAD_BF16,
     CGQA_GRAD_F32,
     CGQA_OK,
@@ -21,6 +24,8 @@ from ._binding import (  # noqa: F401
     attn_naive_fwd,
     attn_naive_workspace_bytes,
     attn_status_string,
+    gemm,
+    gemm_workspace_bytes,
     library,
     library_path,
 )

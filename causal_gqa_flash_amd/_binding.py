@@ -12,6 +12,9 @@ CGQA_EUNSUPPORTED = 2
 CGQA_EHIP = 3
 CGQA_GRAD_F32 = 0
 CGQA_GRAD_BF16 = 1
+CGQA_GEMM_A_KM = 1
+CGQA_GEMM_B_KN = 2
+CGQA_GEMM_C_BF16 = 4
 
 _lib = None
 
@@ -58,6 +61,10 @@ def library():
         lib.attn_naive_fwd.restype = i
         lib.attn_naive_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
         lib.attn_naive_bwd.restype = i
+        lib.cgqa_gemm.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, ctypes.c_size_t, vp]
+        lib.cgqa_gemm_workspace_bytes.argtypes = [i, i, i]
+        lib.cgqa_gemm_workspace_bytes.restype = ctypes.c_size_t
+        lib.cgqa_gemm.restype = i
         lib.attn_status_string.argtypes = [i]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.cgqa_last_hip_error.argtypes = []
@@ -287,3 +294,39 @@ def attn_naive_bwd(q, k, v, do, scale=None, delta=None, dq=None, dk=None, dv=Non
         _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
         ws.numel() * 4, B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
     return delta, dq, dk, dv
+
+
+def gemm_workspace_bytes(M, N, K):
+    return int(library().cgqa_gemm_workspace_bytes(int(M), int(N), int(K)))
+
+
+def gemm(a, b, r=None, c=None, a_km=False, b_kn=False, out_dtype=None, workspace=None, stream=None):
+    """C = A B^T (+ R) on the matrix core. a: bf16 [M, K] (or [K, M] with a_km); b: bf16
+    [N, K] (or [K, N] with b_kn); r: fp32 [M, N] or None (may be c itself); c: output
+    [M, N], fp32 or bf16 (allocated with out_dtype, default fp32, if None); workspace:
+    None or a contiguous fp32 device tensor for splitting long K (gemm_workspace_bytes)."""
+    torch = _torch()
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
+    M, K = (a.shape[1], a.shape[0]) if a_km else (a.shape[0], a.shape[1])
+    N, Kb = (b.shape[1], b.shape[0]) if b_kn else (b.shape[0], b.shape[1])
+    if K != Kb:
+        raise ValueError(f"inner sizes differ: {K} and {Kb}")
+    _need4 = lambda t, name, dt, shape: _need(t.view(1, 1, *t.shape), name, dt, (1, 1) + tuple(shape))
+    _need4(a, "a", torch.bfloat16, a.shape)
+    _need4(b, "b", torch.bfloat16, b.shape)
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a.device)
+    _need4(c, "c", (torch.float32, torch.bfloat16), (M, N))
+    if r is not None:
+        _need4(r, "r", torch.float32, (M, N))
+    flags = (CGQA_GEMM_A_KM if a_km else 0) | (CGQA_GEMM_B_KN if b_kn else 0) | \
+        (CGQA_GEMM_C_BF16 if c.dtype == torch.bfloat16 else 0)
+    ws, wsb = None, 0
+    if workspace is not None:
+        if workspace.dtype != torch.float32 or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous float32 device tensor")
+        ws, wsb = _ptr(workspace), workspace.numel() * 4
+    _check("cgqa_gemm", library().cgqa_gemm(_ptr(a), _ptr(b), _ptr(c), None if r is None else _ptr(r),
+                                            M, N, K, flags, ws, wsb, _stream_ptr(stream)))
+    return c

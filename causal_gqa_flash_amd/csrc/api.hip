@@ -213,9 +213,53 @@ int naive_impl(bool fwd, const uint16_t* q, const uint16_t* k, const uint16_t* v
     return finish(fwd ? cgqa::launch_naive_fwd(a, (hipStream_t)stream) : cgqa::launch_naive_bwd(a, (hipStream_t)stream));
 }
 
+int gemm_impl(const uint16_t* A, const uint16_t* B, void* C, const float* R, int M, int N, int K, int flags,
+              float* ws, size_t ws_bytes, void* stream) {
+    if (M < 0 || N < 0 || K < 0) return CGQA_EINVAL;
+    if (flags & ~(CGQA_GEMM_A_KM | CGQA_GEMM_B_KN | CGQA_GEMM_C_BF16)) return CGQA_EINVAL;
+    const bool akm = flags & CGQA_GEMM_A_KM, bkn = flags & CGQA_GEMM_B_KN, cbf = flags & CGQA_GEMM_C_BF16;
+    const int64_t lim = (int64_t)1 << 31;
+    if ((int64_t)M * K >= lim || (int64_t)N * K >= lim || (int64_t)M * N >= lim) return CGQA_EINVAL;
+    if (K % 32 != 0 || (akm && M % 8 != 0) || (bkn && N % 8 != 0)) return CGQA_EUNSUPPORTED;
+    if (M == 0 || N == 0) return CGQA_OK;
+    if (!C || (K > 0 && (!A || !B))) return CGQA_EINVAL;   // K == 0 reads neither A nor B
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (R && !aligned16(R))) return CGQA_EUNSUPPORTED;
+    if (R && cbf && (const void*)R == C) return CGQA_EINVAL;   // R = C only for an fp32 C
+    const int64_t ceb = cbf ? 2 : 4;
+    const View vc{C, 1, (int64_t)M * N, (int64_t)M * N, ceb};
+    const View va{A, 1, (int64_t)M * K, (int64_t)M * K, 2}, vb{B, 1, (int64_t)N * K, (int64_t)N * K, 2};
+    if (!disjoint(vc, va) || !disjoint(vc, vb)) return CGQA_EINVAL;
+    if (R && (const void*)R != C && !disjoint(vc, View{R, 1, (int64_t)M * N, (int64_t)M * N, 4})) return CGQA_EINVAL;
+    if (ws) {
+        if (!aligned16(ws)) return CGQA_EUNSUPPORTED;
+        const int64_t n = (int64_t)(ws_bytes / 4);
+        const View vw{ws, 1, n > 0 ? n : 1, n > 0 ? n : 1, 4};
+        if (!disjoint(vw, vc) || (K > 0 && (!disjoint(vw, va) || !disjoint(vw, vb))) ||
+            (R && !disjoint(vw, View{R, 1, (int64_t)M * N, (int64_t)M * N, 4})))
+            return CGQA_EINVAL;
+    }
+    cgqa::GemmArgs a{};
+    a.a = A; a.b = B; a.c = C; a.r = R;
+    a.M = M; a.N = N; a.K = K;
+    a.a_km = akm; a.b_kn = bkn; a.c_bf16 = cbf;
+    a.ws = ws; a.ws_bytes = ws ? ws_bytes : 0;
+    return finish(cgqa::launch_gemm(a, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t cgqa_gemm_workspace_bytes(int M, int N, int K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 32 != 0 || (int64_t)M * N >= ((int64_t)1 << 31)) return 0;
+    const int s = cgqa::gemm_splits(M, N, K, (size_t)-1);
+    return s > 1 ? (size_t)s * (size_t)M * (size_t)N * 4 : 0;
+}
+
+int cgqa_gemm(const uint16_t* A, const uint16_t* B, void* C, const float* R, int M, int N, int K, int flags,
+              float* workspace, size_t workspace_bytes, void* stream) {
+    return gemm_impl(A, B, C, R, M, N, K, flags, workspace, workspace_bytes, stream);
+}
 
 size_t attn_naive_workspace_bytes(int B, int T, int Hq) {
     const int64_t n = naive_ws_bytes(B, T, Hq);

@@ -63,6 +63,23 @@ struct NaiveArgs {
     float scale;
 };
 
+// Matrix product C = A B^T (+ R) with layout flags (gemm.hip). K % 32 == 0; A_KM needs
+// M % 8 == 0, B_KN needs N % 8 == 0; M*K, N*K, M*N < 2^31.
+struct GemmArgs {
+    const uint16_t* a;    // [M][K], or [K][M] when a_km
+    const uint16_t* b;    // [N][K], or [K][N] when b_kn
+    void* c;              // [M][N] fp32, or bf16 when c_bf16
+    const float* r;       // [M][N] fp32 added to the product, or null; may be c
+    int M, N, K;
+    int a_km, b_kn, c_bf16;
+    float* ws;            // workspace for a K split, or null (no split)
+    size_t ws_bytes;
+    int tiles_m, tiles_n; // set by the launcher
+    int ksplit, kps;      // set by the launcher: splits of K and 32-k tiles per split
+};
+// Splits of K the launcher uses for this shape and workspace size (1: none).
+int gemm_splits(int M, int N, int K, size_t ws_bytes);
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // Balanced forward for d = 64 and whole 64-query blocks (attn_fwd_split.hip).
 bool fwd_split_supported(const FwdArgs& a);
@@ -72,5 +89,6 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_naive_fwd(const NaiveArgs& a, hipStream_t stream);
 hipError_t launch_naive_bwd(const NaiveArgs& a, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 
 }  // namespace cgqa

@@ -161,6 +161,39 @@ int attn_naive_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, cons
                    float* workspace, size_t workspace_bytes,
                    int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
 
+/* Matrix product of the projections around attention (page "A transformer in PTX",
+ * section "Three ways to run it": one matmul kernel with layout flags, so dx = dy W and
+ * dW = dy^T x run without transposing memory, and with an optional matrix added to the
+ * product, e.g. the residual stream or a gradient accumulated across micro-batches):
+ *
+ *   C[m][n] = sum_k A[m][k] * B[n][k]  (+ R[m][n])
+ *
+ * A is bf16 [M][K] row-major, or [K][M] with CGQA_GEMM_A_KM; B is bf16 [N][K] (a weight
+ * stored [out][in], as x W^T uses it), or [K][N] with CGQA_GEMM_B_KN. C is fp32 [M][N], or
+ * bf16 with CGQA_GEMM_C_BF16 (rounded to nearest even). R is null or fp32 [M][N]; it may
+ * be C itself when C is fp32 (C += A B^T), otherwise it must not overlap C. Products
+ * accumulate in fp32 with k ascending; the bits of C do not depend on the layout flags.
+ *
+ * K must be a multiple of 32; with CGQA_GEMM_A_KM, M a multiple of 8; with CGQA_GEMM_B_KN,
+ * N a multiple of 8 (CGQA_EUNSUPPORTED otherwise). M*K, N*K and M*N must stay below 2^31,
+ * unknown flag bits are CGQA_EINVAL, and C must not overlap A or B. M == 0 or N == 0 is a
+ * no-op; K == 0 writes C = R (or zeros) and then A and B may be null. Same stream,
+ * alignment and error rules as above.
+ *
+ * workspace: null, or caller-owned fp32 device memory of workspace_bytes (16-byte aligned,
+ * overlapping no other argument). Shapes with few 128 x 128 output tiles and a long K (a
+ * weight gradient dW = dy^T x) then split K over several workgroups per tile that write
+ * fp32 partial products there, summed afterwards in split order; at most
+ * cgqa_gemm_workspace_bytes(M, N, K) bytes are used (0: this shape never splits). The
+ * split count, and so the exact bits of C, depend only on M, N, K and workspace_bytes. */
+enum { CGQA_GEMM_A_KM = 1, CGQA_GEMM_B_KN = 2, CGQA_GEMM_C_BF16 = 4 };
+
+size_t cgqa_gemm_workspace_bytes(int M, int N, int K);
+
+int cgqa_gemm(const uint16_t* A, const uint16_t* B, void* C, const float* R,
+              int M, int N, int K, int flags, float* workspace, size_t workspace_bytes,
+              void* stream);
+
 /* Static description of a return code (never NULL). */
 const char* attn_status_string(int status);
 

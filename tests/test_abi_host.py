@@ -316,3 +316,59 @@ def test_naive_empty_problem_is_a_no_op(call):
     n = 6 if call is call_nfwd else 9
     assert call(ptrs=[None] * n, ws_bytes=0, T=0) == cg.CGQA_OK
     assert call(ptrs=[None] * n, ws_bytes=0, B=0) == cg.CGQA_OK
+
+
+# ---- the projection matmul. Every call below is rejected too.
+def call_gemm(ptrs=None, M=64, N=64, K=64, flags=0, ws=None, ws_bytes=0):
+    p = ptrs or [fake(i) for i in range(4)]
+    return cg.library().cgqa_gemm(p[0], p[1], p[2], p[3], M, N, K, flags, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), cg.CGQA_EINVAL), (dict(N=-1), cg.CGQA_EINVAL), (dict(K=-32), cg.CGQA_EINVAL),
+    (dict(flags=8), cg.CGQA_EINVAL), (dict(flags=-1), cg.CGQA_EINVAL),
+    (dict(K=48), cg.CGQA_EUNSUPPORTED), (dict(K=1), cg.CGQA_EUNSUPPORTED),
+    (dict(M=12, flags=cg.CGQA_GEMM_A_KM), cg.CGQA_EUNSUPPORTED),
+    (dict(N=20, flags=cg.CGQA_GEMM_B_KN), cg.CGQA_EUNSUPPORTED),
+    (dict(M=1 << 16, K=1 << 15), cg.CGQA_EINVAL), (dict(N=1 << 16, K=1 << 15), cg.CGQA_EINVAL),
+    (dict(M=1 << 16, N=1 << 15), cg.CGQA_EINVAL),
+])
+def test_gemm_bad_sizes_rejected(kw, code):
+    assert call_gemm(**kw) == code
+
+
+def test_gemm_bad_pointers_rejected():
+    for i in range(3):                         # A, B, C; R may be null
+        p = [fake(j) for j in range(4)]
+        p[i] = None
+        assert call_gemm(ptrs=p) == cg.CGQA_EINVAL, i
+    for i in range(4):
+        p = [fake(j) for j in range(4)]
+        p[i] += 8
+        assert call_gemm(ptrs=p) == cg.CGQA_EUNSUPPORTED, i
+    # C overlapping A or B, or R overlapping C without being C
+    for other in (0, 1, 3):
+        p = [fake(j) for j in range(4)]
+        p[2] = p[other] + 64
+        assert call_gemm(ptrs=p) == cg.CGQA_EINVAL, other
+    # R == C needs an fp32 C
+    p = [fake(j) for j in range(4)]
+    p[3] = p[2]
+    assert call_gemm(ptrs=p, flags=cg.CGQA_GEMM_C_BF16) == cg.CGQA_EINVAL
+
+
+def test_gemm_empty_is_a_no_op():
+    assert call_gemm(ptrs=[None] * 4, M=0) == cg.CGQA_OK
+    assert call_gemm(ptrs=[None] * 4, N=0) == cg.CGQA_OK
+
+
+def test_gemm_workspace_rules():
+    # misaligned or overlapping workspaces are rejected before any HIP call
+    assert call_gemm(ws=fake(5) + 8, ws_bytes=1 << 20) == cg.CGQA_EUNSUPPORTED
+    for other in range(4):
+        assert call_gemm(ws=fake(other) + 64, ws_bytes=1 << 20) == cg.CGQA_EINVAL, other
+    # size query: long K over few tiles splits; many tiles or short K do not
+    assert cg.gemm_workspace_bytes(640, 384, 16384) == 32 * 640 * 384 * 4
+    assert cg.gemm_workspace_bytes(16384, 640, 384) == 0
+    assert cg.gemm_workspace_bytes(640, 384, 256) == 0
+    assert cg.gemm_workspace_bytes(640, 384, 100) == 0
