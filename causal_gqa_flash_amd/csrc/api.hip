@@ -253,7 +253,7 @@ extern "C" {
 size_t cgqa_gemm_workspace_bytes(int M, int N, int K) {
     if (M <= 0 || N <= 0 || K <= 0 || K % 32 != 0 || (int64_t)M * N >= ((int64_t)1 << 31)) return 0;
     const int s = cgqa::gemm_splits(M, N, K, (size_t)-1);
-    return s > 1 ? (size_t)s * (size_t)M * (size_t)N * 4 : 0;
+    return s > 1 ? (size_t)s * cgqa::gemm_slice_floats(M, N) * 4 : 0;
 }
 
 int cgqa_gemm(const uint16_t* A, const uint16_t* B, void* C, const float* R, int M, int N, int K, int flags,

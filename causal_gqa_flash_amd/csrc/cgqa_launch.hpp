@@ -79,6 +79,8 @@ struct GemmArgs {
 };
 // Splits of K the launcher uses for this shape and workspace size (1: none).
 int gemm_splits(int M, int N, int K, size_t ws_bytes);
+// Floats per split's partial product in the workspace: M*N rounded up to a multiple of 4.
+__host__ __device__ inline size_t gemm_slice_floats(int M, int N) { return ((size_t)M * N + 3) & ~(size_t)3; }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // Balanced forward for d = 64 and whole 64-query blocks (attn_fwd_split.hip).

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 3) void gemm_bf16_kernel(GemmArgs a) {
     }
 
     // Epilogue: with a K split the fp32 partial goes to the workspace slice of this split.
-    float* const part = a.ksplit > 1 ? a.ws + (size_t)split * a.M * a.N : nullptr;
+    float* const part = a.ksplit > 1 ? a.ws + (size_t)split * gemm_slice_floats(a.M, a.N) : nullptr;
     const bool full = m0 + kBM <= a.M && n0 + kBN <= a.N;   // no bounds checks needed
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
@@ -232,12 +232,13 @@ __global__ __launch_bounds__(kThreads, 3) void gemm_bf16_kernel(GemmArgs a) {
         }
 }
 
-// C = sum over splits s = 0 .. S-1 (in order) of the partials, + R.
+// C = sum over splits s = 0 .. S-1 (in order) of the partials, + R. Four consecutive
+// elements per thread (slices are padded to a multiple of four floats), eight partials in
+// flight; the tail of M*N that is not a whole group of four goes one element at a time.
 __global__ __launch_bounds__(kThreads) void gemm_splitk_sum_kernel(GemmArgs a) {
-    const size_t mn = (size_t)a.M * a.N;
-    for (size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x; idx < mn; idx += (size_t)gridDim.x * kThreads) {
-        float x = a.ws[idx];
-        for (int s = 1; s < a.ksplit; ++s) x += a.ws[(size_t)s * mn + idx];
+    const size_t mn = (size_t)a.M * a.N, slice = gemm_slice_floats(a.M, a.N), n4 = mn / 4;
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    auto finish_store = [&](float x, size_t idx) CGQA_INLINE {
         if (a.r) x += a.r[idx];
         if (a.c_bf16) {
             const uint32_t u = __float_as_uint(x);
@@ -245,6 +246,25 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_sum_kernel(GemmArgs a) {
         } else {
             static_cast<float*>(a.c)[idx] = x;
         }
+    };
+    for (size_t q = (size_t)blockIdx.x * kThreads + threadIdx.x; q < n4; q += stride) {
+        f32x4 x = *reinterpret_cast<const f32x4*>(a.ws + 4 * q);
+        int s = 1;
+        for (; s + 8 <= a.ksplit; s += 8) {
+            f32x4 y[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) y[u] = *reinterpret_cast<const f32x4*>(a.ws + (size_t)(s + u) * slice + 4 * q);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x += y[u];
+        }
+        for (; s < a.ksplit; ++s) x += *reinterpret_cast<const f32x4*>(a.ws + (size_t)s * slice + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) finish_store(x[e], 4 * q + e);
+    }
+    for (size_t idx = 4 * n4 + (size_t)blockIdx.x * kThreads + threadIdx.x; idx < mn; idx += stride) {
+        float x = a.ws[idx];
+        for (int s = 1; s < a.ksplit; ++s) x += a.ws[(size_t)s * slice + idx];
+        finish_store(x, idx);
     }
 }
 
@@ -260,7 +280,7 @@ int gemm_splits(int M, int N, int K, size_t ws_bytes) {
     long s = (512 + tiles - 1) / tiles;
     s = s < nk / 8 ? s : nk / 8;
     s = s < 32 ? s : 32;
-    const size_t per = (size_t)M * N * 4;
+    const size_t per = gemm_slice_floats(M, N) * 4;
     if ((size_t)s * per > ws_bytes) s = (long)(ws_bytes / per);
     if (s < 2) return 1;
     const int kps = (nk + (int)s - 1) / (int)s;
@@ -284,8 +304,8 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t stream) {
     else if (!a.b_kn) hipLaunchKernelGGL((gemm_bf16_kernel<true, false>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((gemm_bf16_kernel<true, true>), grid, block, 0, stream, a);
     if (a.ksplit > 1) {
-        const size_t mn = (size_t)a.M * a.N;
-        const unsigned sb = (unsigned)((mn + kThreads - 1) / kThreads < 4096 ? (mn + kThreads - 1) / kThreads : 4096);
+        const size_t groups = ((size_t)a.M * a.N + 3) / 4;
+        const unsigned sb = (unsigned)((groups + kThreads - 1) / kThreads < 4096 ? (groups + kThreads - 1) / kThreads : 4096);
         hipLaunchKernelGGL(gemm_splitk_sum_kernel, dim3(sb), dim3(kThreads), 0, stream, a);
     }
     return hipGetLastError();

@@ -369,6 +369,7 @@ def test_gemm_workspace_rules():
         assert call_gemm(ws=fake(other) + 64, ws_bytes=1 << 20) == cg.CGQA_EINVAL, other
     # size query: long K over few tiles splits; many tiles or short K do not
     assert cg.gemm_workspace_bytes(640, 384, 16384) == 32 * 640 * 384 * 4
+    assert cg.gemm_workspace_bytes(1, 1, 1024) == 4 * 4 * 4          # slices padded to 4 floats
     assert cg.gemm_workspace_bytes(16384, 640, 384) == 0
     assert cg.gemm_workspace_bytes(640, 384, 256) == 0
     assert cg.gemm_workspace_bytes(640, 384, 100) == 0
