@@ -107,3 +107,14 @@ def slice_group(arrs, Hq, Hkv, b, g):
         else:
             out[name] = np.ascontiguousarray(a[b:b + 1, :, g:g + 1, :])
     return out
+
+
+def rope_tables(T, d, base=10000.0):
+    """Rotary position tables, inputs of the RoPE calls: cos and sin of t * base^(-2i/d)
+    for positions t < T and pairs i < d/2 (angles in float64, rounded once to float32),
+    each float32 [T][d/2]. The usual Llama choice of frequencies; the calls take any
+    table."""
+    t = np.arange(T, dtype=np.float64)[:, None]
+    inv = base ** (-np.arange(0, d, 2, dtype=np.float64) / d)[None, :]
+    ang = t * inv
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
