@@ -66,3 +66,44 @@ def test_rotate_bf16_rounds_the_rotated_value():
     assert np.all(np.abs(r - exact) <= 2.0 ** -8 * np.abs(exact) + 1e-30)
     # and every value is a bf16 number (widening its bits gives it back)
     assert np.array_equal(si.bf16_bits_to_f32(si.f32_to_bf16_bits(r.astype(np.float32))), r.astype(np.float32))
+
+
+def test_fma32_is_the_exact_value_rounded_once():
+    from fractions import Fraction
+    rng = np.random.default_rng(24)
+    a = rng.standard_normal(3000).astype(np.float32)
+    b = rng.standard_normal(3000).astype(np.float32)
+    c = (rng.standard_normal(3000) * 10.0 ** rng.integers(-8, 3, 3000)).astype(np.float32)
+    # constructed halfway cases: a*b lands exactly between two float32 numbers next to c
+    for i in range(0, 200):
+        c[i] = np.float32(1.0)
+        a[i] = np.float32(1.0)
+        b[i] = np.float32(2.0 ** -24 * (1 + 2 * (i % 2)))   # 1 + 2^-24 (tie) or 1 + 3 * 2^-24
+    got = rope.fma32(a, b, c)
+
+    def round32(fr):
+        # nearest float32 to a Fraction (ties to even), by bracketing with nextafter
+        f = np.float32(float(fr))
+        lo, hi = (f, np.nextafter(f, np.float32(np.inf))) if Fraction(float(f)) <= fr else \
+                 (np.nextafter(f, np.float32(-np.inf)), f)
+        dlo, dhi = fr - Fraction(float(lo)), Fraction(float(hi)) - fr
+        if dlo < dhi:
+            return lo
+        if dhi < dlo:
+            return hi
+        return lo if (int(np.float32(lo).view(np.uint32)) & 1) == 0 else hi
+
+    for i in range(len(a)):
+        exact = Fraction(float(a[i])) * Fraction(float(b[i])) + Fraction(float(c[i]))
+        assert got[i] == round32(exact), (i, a[i], b[i], c[i], got[i])
+
+
+def test_fp32_rotation_rounds_like_the_exact_one_almost_always():
+    rng = np.random.default_rng(25)
+    x = si.f32_to_bf16_bits(rng.standard_normal((2, 64, 3, 64), dtype=np.float32))
+    cos, sin = si.rope_tables(64, 64)
+    a = rope.rotate_bf16_fp32(x, cos, sin)
+    b = rope.rotate_bf16(x, cos, sin)
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(b), 1e-30))) - 7)
+    assert np.all(np.abs(a - b) <= ulp)
+    assert np.mean(a == b) > 0.99
