@@ -208,6 +208,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-naive", action="store_true", help="skip timing the naive reference mode")
     ap.add_argument("--no-gemm", action="store_true", help="skip timing the projection matmuls")
+    ap.add_argument("--no-rope", action="store_true", help="skip timing the rotary embedding")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="run the short workload that rocprofv3 --pmc profiles (see profiles/)")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -353,6 +354,27 @@ def main():
         del ws
     if not args.no_gemm:
         out["gemm"] = gemm_bench(w, timed, stream)
+    if not args.no_rope:
+        # Rotary embedding: the rotation pass of Q and K (HBM-bound: each element read and
+        # written once, plus the tables), and the backward with dQ, dK turned back inside.
+        c_np, s_np = si.rope_tables(w.T, w.d)
+        rc, rs = torch.from_numpy(c_np).cuda(), torch.from_numpy(s_np).cuda()
+        q_rot = torch.empty_like(q)
+        k_rot = torch.empty_like(k)
+        def rope_pass():
+            cg.rope_qk(q, k, rc, rs, q_out=q_rot, k_out=k_rot, stream=stream)
+        def bwd_rope():
+            cg.attn_bwd_dq(q, k, v, o, do, lse, scale=w.scale, delta=delta, dq=dq, stream=stream, rope=(rc, rs))
+            cg.attn_bwd_dkv(q, k, v, do, lse, delta, scale=w.scale, dk=dk, dv=dv, stream=stream, rope=(rc, rs))
+        rope_pass(); bwd_rope()
+        torch.cuda.synchronize()
+        ms_rope, ms_bwd_rope = timed(rope_pass, args.steps), timed(bwd_rope, args.steps)
+        rope_bytes = 2 * 2 * w.B * w.T * (w.Hq + w.Hkv) * w.d + 2 * 4 * w.T * (w.d // 2)
+        gbs = rope_bytes / (ms_rope * 1e-3) / 1e9
+        out["rope"] = {"pass_ms": round(ms_rope, 5), "bytes": rope_bytes,
+                       "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)},
+                       "bwd_ms": round(ms_bwd_rope, 5), "bwd_plain_ms": round(bwd_ms, 5)}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)

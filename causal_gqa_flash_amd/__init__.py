@@ -28,4 +28,5 @@ from ._binding import (  # noqa: F401
     gemm_workspace_bytes,
     library,
     library_path,
+    rope_qk,
 )

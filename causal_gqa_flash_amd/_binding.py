@@ -62,6 +62,12 @@ def library():
         lib.attn_naive_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
         lib.attn_naive_bwd.restype = i
         lib.cgqa_gemm.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, ctypes.c_size_t, vp]
+        lib.attn_rope_qk.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp]
+        lib.attn_rope_qk.restype = i
+        lib.attn_bwd_dq_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.attn_bwd_dq_rope.restype = i
+        lib.attn_bwd_dkv_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.attn_bwd_dkv_rope.restype = i
         lib.cgqa_gemm_workspace_bytes.argtypes = [i, i, i]
         lib.cgqa_gemm_workspace_bytes.restype = ctypes.c_size_t
         lib.cgqa_gemm.restype = i
@@ -173,9 +179,19 @@ def _grad_code(dtype):
     return CGQA_GRAD_BF16 if dtype == torch.bfloat16 else CGQA_GRAD_F32
 
 
-def attn_bwd_dq(q, k, v, o, do, lse, scale=None, delta=None, dq=None, stream=None, grad_dtype=None):
+def _rope_tables(rope, T, d):
+    torch = _torch()
+    cos, sin = rope
+    for t, name in ((cos, "rope cos"), (sin, "rope sin")):
+        _need(t.view(1, 1, *t.shape), name, torch.float32, (1, 1, T, d // 2))
+    return cos, sin
+
+
+def attn_bwd_dq(q, k, v, o, do, lse, scale=None, delta=None, dq=None, stream=None, grad_dtype=None, rope=None):
     """delta [B,Hq,T] fp32 and dq [B,T,Hq,d], fp32 or bf16 (the dtype of the dq given,
-    else grad_dtype, else fp32). Inputs and dq may be row-strided views."""
+    else grad_dtype, else fp32). Inputs and dq may be row-strided views. With
+    rope=(cos, sin) (fp32 [T, d/2]), q and k are the rotated tensors and dq is returned
+    with respect to the unrotated q (contiguous tensors, fp32 dq)."""
     torch = _torch()
     B, T, Hq, Hkv, d = _dims(q, k)
     rq, ro, rdo = (_need(t, name, torch.bfloat16, (B, T, Hq, d), rows=True)
@@ -190,7 +206,15 @@ def attn_bwd_dq(q, k, v, o, do, lse, scale=None, delta=None, dq=None, stream=Non
     _need(delta, "delta", torch.float32, (B, Hq, T))
     rdq = _need(dq, "dq", (torch.float32, torch.bfloat16), (B, T, Hq, d), rows=True)
     lib = library()
-    if (rq, rkv, ro, rdo, rdq) == (Hq * d, Hkv * d, Hq * d, Hq * d, Hq * d) and dq.dtype == torch.float32:
+    contiguous = (rq, rkv, ro, rdo, rdq) == (Hq * d, Hkv * d, Hq * d, Hq * d, Hq * d)
+    if rope is not None:
+        if not contiguous or dq.dtype != torch.float32:
+            raise ValueError("the rotary backward takes contiguous tensors and an fp32 dq")
+        cos, sin = _rope_tables(rope, T, d)
+        _check("attn_bwd_dq_rope", lib.attn_bwd_dq_rope(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(cos), _ptr(sin),
+            B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
+    elif contiguous and dq.dtype == torch.float32:
         _check("attn_bwd_dq", lib.attn_bwd_dq(
             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq),
             B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
@@ -201,10 +225,12 @@ def attn_bwd_dq(q, k, v, o, do, lse, scale=None, delta=None, dq=None, stream=Non
     return delta, dq
 
 
-def attn_bwd_dkv(q, k, v, do, lse, delta, scale=None, dk=None, dv=None, stream=None, grad_dtype=None):
+def attn_bwd_dkv(q, k, v, do, lse, delta, scale=None, dk=None, dv=None, stream=None, grad_dtype=None, rope=None):
     """dk, dv [B,T,Hkv,d], fp32 or bf16 (the dtype of the dk/dv given, else grad_dtype,
     else fp32). Enqueue after attn_bwd_dq on the same stream. Inputs and dk, dv may be
-    row-strided views (dk and dv with one row stride)."""
+    row-strided views (dk and dv with one row stride). With rope=(cos, sin), q and k are
+    the rotated tensors and dk is returned with respect to the unrotated k (contiguous
+    tensors, fp32 gradients)."""
     torch = _torch()
     B, T, Hq, Hkv, d = _dims(q, k)
     rq, rdo = (_need(t, name, torch.bfloat16, (B, T, Hq, d), rows=True) for t, name in ((q, "q"), (do, "do")))
@@ -223,7 +249,15 @@ def attn_bwd_dkv(q, k, v, do, lse, delta, scale=None, dk=None, dv=None, stream=N
     if rdk != rdv:
         raise ValueError(f"dk and dv must share one row stride, got {rdk} and {rdv}")
     lib = library()
-    if (rq, rkv, rdo, rdk) == (Hq * d, Hkv * d, Hq * d, Hkv * d) and dk.dtype == torch.float32:
+    contiguous = (rq, rkv, rdo, rdk) == (Hq * d, Hkv * d, Hq * d, Hkv * d)
+    if rope is not None:
+        if not contiguous or dk.dtype != torch.float32:
+            raise ValueError("the rotary backward takes contiguous tensors and fp32 dk, dv")
+        cos, sin = _rope_tables(rope, T, d)
+        _check("attn_bwd_dkv_rope", lib.attn_bwd_dkv_rope(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv), _ptr(cos), _ptr(sin),
+            B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
+    elif contiguous and dk.dtype == torch.float32:
         _check("attn_bwd_dkv", lib.attn_bwd_dkv(
             _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
             B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
@@ -330,3 +364,24 @@ def gemm(a, b, r=None, c=None, a_km=False, b_kn=False, out_dtype=None, workspace
     _check("cgqa_gemm", library().cgqa_gemm(_ptr(a), _ptr(b), _ptr(c), None if r is None else _ptr(r),
                                             M, N, K, flags, ws, wsb, _stream_ptr(stream)))
     return c
+
+
+def rope_qk(q, k, cos, sin, q_out=None, k_out=None, stream=None):
+    """Rotary embedding of bf16 q [B,T,Hq,d] and k [B,T,Hkv,d] with fp32 tables cos, sin
+    [T, d/2]: returns (q_out, k_out), bf16. Tensors may be row-strided views; q_out=q and
+    k_out=k rotate in place (e.g. inside a packed QKV buffer)."""
+    torch = _torch()
+    B, T, Hq, Hkv, d = _dims(q, k)
+    rq = _need(q, "q", torch.bfloat16, (B, T, Hq, d), rows=True)
+    rk = _need(k, "k", torch.bfloat16, (B, T, Hkv, d), rows=True)
+    if q_out is None:
+        q_out = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if k_out is None:
+        k_out = torch.empty((B, T, Hkv, d), dtype=torch.bfloat16, device=q.device)
+    rqo = _need(q_out, "q_out", torch.bfloat16, (B, T, Hq, d), rows=True)
+    rko = _need(k_out, "k_out", torch.bfloat16, (B, T, Hkv, d), rows=True)
+    cos, sin = _rope_tables((cos, sin), T, d)
+    _check("attn_rope_qk", library().attn_rope_qk(
+        _ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(cos), _ptr(sin), B, T, Hq, Hkv, d,
+        rq, rk, rqo, rko, _stream_ptr(stream)))
+    return q_out, k_out

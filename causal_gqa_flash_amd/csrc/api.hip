@@ -104,7 +104,8 @@ struct BwdStrides {
 int bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
              const uint16_t* dO, const float* lse, const float* delta_in, float* delta_out,
              void* dq, void* dk, void* dv, int B, int T, int Hq, int Hkv, int d, const BwdStrides& st,
-             float scale, void* stream, bool is_dq) {
+             float scale, void* stream, bool is_dq, const float* rope_cos = nullptr,
+             const float* rope_sin = nullptr) {
     bool empty = false;
     int rc = check_shape(B, T, Hq, Hkv, d, scale, &empty);
     if (rc != CGQA_OK) return rc;
@@ -145,8 +146,20 @@ int bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
         for (const View& s : ins)
             if (!disjoint(s, outs[0]) || !disjoint(s, outs[1])) return CGQA_EINVAL;
     }
+    if (rope_cos || rope_sin) {
+        if (!rope_cos || !rope_sin) return CGQA_EINVAL;
+        if (!aligned16(rope_cos) || !aligned16(rope_sin)) return CGQA_EUNSUPPORTED;
+        const int64_t nt = (int64_t)T * (d / 2);
+        const View vc{rope_cos, 1, nt, nt, 4}, vs{rope_sin, 1, nt, nt, 4};
+        const View outs[3] = {is_dq ? View{delta_out, 1, nr, nr, 4} : View{dk, rows, wkv, st.dkv_rs, geb},
+                              is_dq ? View{dq, rows, wq, st.dq_rs, geb} : View{dv, rows, wkv, st.dkv_rs, geb},
+                              vc};
+        for (int x = 0; x < 2; ++x)
+            if (!disjoint(outs[x], vc) || !disjoint(outs[x], vs)) return CGQA_EINVAL;
+    }
     cgqa::BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
+    a.rope_cos = rope_cos; a.rope_sin = rope_sin;
     a.delta = is_dq ? delta_out : const_cast<float*>(delta_in);
     a.dq = dq; a.dk = dk; a.dv = dv;
     a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
@@ -249,6 +262,64 @@ int gemm_impl(const uint16_t* A, const uint16_t* B, void* C, const float* R, int
 }  // namespace
 
 extern "C" {
+
+int attn_rope_qk(const uint16_t* q, const uint16_t* k, uint16_t* q_out, uint16_t* k_out, const float* cos_t,
+                 const float* sin_t, int B, int T, int Hq, int Hkv, int d, int q_row_stride, int k_row_stride,
+                 int q_out_row_stride, int k_out_row_stride, void* stream) {
+    bool empty = false;
+    int rc = check_shape(B, T, Hq, Hkv, d, 1.0f, &empty);
+    if (rc != CGQA_OK) return rc;
+    const int64_t rows = (int64_t)B * T, wq = (int64_t)Hq * d, wk = (int64_t)Hkv * d;
+    const int64_t rcs[4] = {check_stride(q_row_stride, wq, rows, 8), check_stride(k_row_stride, wk, rows, 8),
+                            check_stride(q_out_row_stride, wq, rows, 8), check_stride(k_out_row_stride, wk, rows, 8)};
+    for (int64_t r : rcs)
+        if (r == CGQA_EINVAL) return CGQA_EINVAL;
+    for (int64_t r : rcs)
+        if (r != CGQA_OK) return (int)r;
+    if (empty) return CGQA_OK;
+    if (!q || !k || !q_out || !k_out || !cos_t || !sin_t) return CGQA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out) || !aligned16(cos_t) ||
+        !aligned16(sin_t))
+        return CGQA_EUNSUPPORTED;
+    const int64_t nt = (int64_t)T * (d / 2);
+    const View vq{q, rows, wq, q_row_stride, 2}, vk{k, rows, wk, k_row_stride, 2},
+        vqo{q_out, rows, wq, q_out_row_stride, 2}, vko{k_out, rows, wk, k_out_row_stride, 2},
+        vc{cos_t, 1, nt, nt, 4}, vs{sin_t, 1, nt, nt, 4};
+    // An output may be its own input exactly (in place); otherwise nothing may overlap it.
+    const bool q_inplace = q_out == q && q_out_row_stride == q_row_stride;
+    const bool k_inplace = k_out == k && k_out_row_stride == k_row_stride;
+    if (!disjoint(vqo, vko) || !disjoint(vqo, vk) || !disjoint(vko, vq)) return CGQA_EINVAL;
+    if ((!q_inplace && !disjoint(vqo, vq)) || (!k_inplace && !disjoint(vko, vk))) return CGQA_EINVAL;
+    for (const View& o : {vqo, vko})
+        if (!disjoint(o, vc) || !disjoint(o, vs)) return CGQA_EINVAL;
+    cgqa::RopeArgs a{};
+    a.q = q; a.k = k; a.q_out = q_out; a.k_out = k_out; a.cos = cos_t; a.sin = sin_t;
+    a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+    a.q_rs = q_row_stride; a.k_rs = k_row_stride; a.qo_rs = q_out_row_stride; a.ko_rs = k_out_row_stride;
+    return finish(cgqa::launch_rope(a, (hipStream_t)stream));
+}
+
+int attn_bwd_dq_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                     const uint16_t* dO, const float* lse, float* delta, float* dq, const float* rope_cos,
+                     const float* rope_sin, int B, int T, int Hq, int Hkv, int d, float scale, void* stream) {
+    const int64_t wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d;
+    if (Hq < 1 || Hkv < 1 || wq >= ((int64_t)1 << 31)) return CGQA_EINVAL;
+    if (!rope_cos || !rope_sin) return CGQA_EINVAL;
+    const BwdStrides st{(int)wq, (int)wkv, (int)wq, (int)wq, (int)wq, (int)wkv, CGQA_GRAD_F32};
+    return bwd_impl(q, k, v, o, dO, lse, nullptr, delta, dq, nullptr, nullptr, B, T, Hq, Hkv, d, st, scale,
+                    stream, true, rope_cos, rope_sin);
+}
+
+int attn_bwd_dkv_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
+                      const float* lse, const float* delta, float* dk, float* dv, const float* rope_cos,
+                      const float* rope_sin, int B, int T, int Hq, int Hkv, int d, float scale, void* stream) {
+    const int64_t wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d;
+    if (Hq < 1 || Hkv < 1 || wq >= ((int64_t)1 << 31)) return CGQA_EINVAL;
+    if (!rope_cos || !rope_sin) return CGQA_EINVAL;
+    const BwdStrides st{(int)wq, (int)wkv, (int)wq, (int)wq, (int)wq, (int)wkv, CGQA_GRAD_F32};
+    return bwd_impl(q, k, v, nullptr, dO, lse, delta, nullptr, nullptr, dk, dv, B, T, Hq, Hkv, d, st, scale,
+                    stream, false, rope_cos, rope_sin);
+}
 
 size_t cgqa_gemm_workspace_bytes(int M, int N, int K) {
     if (M <= 0 || N <= 0 || K <= 0 || K % 32 != 0 || (int64_t)M * N >= ((int64_t)1 << 31)) return 0;

@@ -261,6 +261,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     x[r] = a.scale * fmaf(-corr, kbar[qb][mb][4 * u + r], dqacc[qb][mb][4 * u + r]);
+                if (a.rope_cos) x = rope_back4(x, a.rope_cos, a.rope_sin, query, D / 2, 32 * mb + 8 * u + 4 * hl);
                 store_out4(a.dq, drow + 32 * mb + 8 * u + 4 * hl, x, a.grad_bf16);
             }
     }
@@ -317,9 +318,9 @@ struct DkvCfg {
 
 // SAME_QDO: Q and dO have the same row stride (every contiguous call), so their DMA
 // shares one set of lane offsets and one cursor offset. BF16OUT: dK and dV are written
-// as bf16 (a compile-time choice: a run-time one costs this kernel registers it has not
-// got).
-template <int D, int BQ, int NKW, int HS, int NR, bool SAME_QDO, bool BF16OUT>
+// as bf16. ROPE: dK is turned back by the rotary tables. (Compile-time choices: run-time
+// ones cost this kernel registers it has not got.)
+template <int D, int BQ, int NKW, int HS, int NR, bool SAME_QDO, bool BF16OUT, bool ROPE>
 __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) {
     using C = DkvCfg<D, BQ, NKW, HS, NR>;
     __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
@@ -607,7 +608,8 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     // 16-byte access of a wave covers 1 KB of consecutive LDS (no bank conflicts).
     float* red = reinterpret_cast<float*>(smem);
     auto red_at = [&](int slot, int u) { return red + (size_t)((((slot - 1) * NKW + pos) * 4 + u) * 64 + lane) * 4; };
-    auto reduce_store = [&](f32x16 (&acc)[C::kMB], void* out, float mul) {
+    auto reduce_store = [&](f32x16 (&acc)[C::kMB], void* out, float mul, auto Rc) {
+        constexpr bool ROT = decltype(Rc)::value;
 #pragma unroll
         for (int mb = 0; mb < C::kMB; ++mb) {
             if (HS > 1) {
@@ -641,13 +643,14 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
                     f32x4 x;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) x[r] = acc[mb][4 * u + r] * mul;
+                    if constexpr (ROT) x = rope_back4(x, a.rope_cos, a.rope_sin, key, D / 2, 32 * mb + 8 * u + 4 * hl);
                     store_out4(out, row + 32 * mb + 8 * u + 4 * hl, x, BF16OUT);
                 }
             }
         }
     };
-    reduce_store(dkacc, a.dk, a.scale);
-    reduce_store(dvacc, a.dv, 1.0f);
+    reduce_store(dkacc, a.dk, a.scale, std::integral_constant<bool, ROPE>{});
+    reduce_store(dvacc, a.dv, 1.0f, std::false_type{});
 }
 
 // ---- Software-pipelined dQ (d = 64) ---------------------------------------------------
@@ -902,6 +905,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
                 f32x4 x;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) x[r] = a.scale * fmaf(-corr, kbar[mb][4 * u + r], dqacc[mb][4 * u + r]);
+                if (a.rope_cos) x = rope_back4(x, a.rope_cos, a.rope_sin, query, D / 2, 32 * mb + 8 * u + 4 * hl);
                 store_out4(a.dq, drow + 32 * mb + 8 * u + 4 * hl, x, a.grad_bf16);
             }
     }
@@ -938,14 +942,17 @@ static hipError_t launch_dkv_t(const BwdArgs& a, hipStream_t stream) {
     x.zigzag = blocks <= 256 ? 1 : 0;
     const dim3 grid((unsigned)blocks), block(C::kThreads);
     const bool same = a.q_rs == a.do_rs;
-    if (same && !a.grad_bf16)
-        hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR, true, false>), grid, block, 0, stream, x);
+    if (a.rope_cos) {
+        // Rotary calls come contiguous (same Q and dO stride) with fp32 gradients.
+        hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR, true, false, true>), grid, block, 0, stream, x);
+    } else if (same && !a.grad_bf16)
+        hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR, true, false, false>), grid, block, 0, stream, x);
     else if (same)
-        hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR, true, true>), grid, block, 0, stream, x);
+        hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR, true, true, false>), grid, block, 0, stream, x);
     else if (!a.grad_bf16)
-        hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR, false, false>), grid, block, 0, stream, x);
+        hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR, false, false, false>), grid, block, 0, stream, x);
     else
-        hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR, false, true>), grid, block, 0, stream, x);
+        hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, BQ, NKW, HS, NR, false, true, false>), grid, block, 0, stream, x);
     return hipGetLastError();
 }
 

@@ -39,6 +39,8 @@ struct BwdArgs {
     int q_rs, kv_rs, o_rs, do_rs;   // input row strides (elements)
     int dq_rs, dkv_rs;              // output row strides (elements of the output type)
     int grad_bf16;                  // 1: dQ, dK, dV rounded to bf16 (nearest even)
+    const float* rope_cos;          // rotary tables [T][d/2]: dQ and dK are turned back to
+    const float* rope_sin;          // the unrotated inputs' frame (null: no rotation)
     float scale;        // softmax scale (dS carries it into dQ and dK)
     float scale_log2;   // scale * log2(e)
     int n_tiles;        // set by the launcher
@@ -81,6 +83,19 @@ struct GemmArgs {
 int gemm_splits(int M, int N, int K, size_t ws_bytes);
 // Floats per split's partial product in the workspace: M*N rounded up to a multiple of 4.
 __host__ __device__ inline size_t gemm_slice_floats(int M, int N) { return ((size_t)M * N + 3) & ~(size_t)3; }
+
+// Rotary embedding of Q and K (rope.hip): out = R(t) in per pair, bf16.
+struct RopeArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    uint16_t* q_out;      // may be q itself (same stride)
+    uint16_t* k_out;      // may be k itself
+    const float* cos;     // [T][d/2]
+    const float* sin;
+    int B, T, Hq, Hkv, d;
+    int q_rs, k_rs, qo_rs, ko_rs;   // row strides (elements)
+};
+hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // Balanced forward for d = 64 and whole 64-query blocks (attn_fwd_split.hip).

@@ -133,6 +133,39 @@ int attn_bwd_dkv_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          int q_row_stride, int kv_row_stride, int do_row_stride,
                          int dkv_row_stride, int grad_dtype, float scale, void* stream);
 
+/* Rotary position embedding around attention (page "A transformer in PTX", section "The
+ * model": the fused QKV matmul's queries and keys are rotated with RoPE, in place in the
+ * bf16 buffer, before causal attention). Pair i = (x[2i], x[2i+1]) of every head of token
+ * t turns by the angle whose cosine and sine are cos[t][i] and sin[t][i] (caller tables,
+ * fp32 [T][d/2], 16-byte aligned):
+ *   y[2i] = x[2i] cos - x[2i+1] sin,   y[2i+1] = x[2i] sin + x[2i+1] cos.
+ *
+ * attn_rope_qk writes the rotated q and k as bf16 (computed in fp32, rounded to nearest
+ * even); tensors are [B][T][H][d] with row strides as in the strided calls (multiples of
+ * 8). An output may be its own input (same pointer and stride: in place, e.g. on the packed
+ * QKV buffer); any other overlap of an output is CGQA_EINVAL. The forward then runs
+ * attn_fwd on the rotated tensors.
+ *
+ * attn_bwd_dq_rope / attn_bwd_dkv_rope are attn_bwd_dq / attn_bwd_dkv on the rotated q and k
+ * (contiguous, fp32 gradients) whose dq and dk are turned back inside the kernels, before
+ * they are stored, to the gradients with respect to the unrotated q and k:
+ *   g[2i] = gy[2i] cos + gy[2i+1] sin,   g[2i+1] = -gy[2i] sin + gy[2i+1] cos
+ * (dv and delta are unchanged). */
+int attn_rope_qk(const uint16_t* q, const uint16_t* k, uint16_t* q_out, uint16_t* k_out,
+                 const float* cos, const float* sin, int B, int T, int Hq, int Hkv, int d,
+                 int q_row_stride, int k_row_stride, int q_out_row_stride, int k_out_row_stride,
+                 void* stream);
+
+int attn_bwd_dq_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     const uint16_t* o, const uint16_t* dO, const float* lse,
+                     float* delta, float* dq, const float* cos, const float* sin,
+                     int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
+
+int attn_bwd_dkv_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* dO, const float* lse, const float* delta,
+                      float* dk, float* dv, const float* cos, const float* sin,
+                      int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
+
 /* Naive attention, the GPU reference mode (page "A transformer in PTX", section "Three
  * ways to run it": the fast kernels are checked against naive ones; section "Flash
  * attention": naive kernels store the whole T x T score matrix of every head). Same

@@ -373,3 +373,55 @@ def test_gemm_workspace_rules():
     assert cg.gemm_workspace_bytes(16384, 640, 384) == 0
     assert cg.gemm_workspace_bytes(640, 384, 256) == 0
     assert cg.gemm_workspace_bytes(640, 384, 100) == 0
+
+
+
+# ---- rotary embedding. Every call below is rejected too.
+def call_rope(ptrs=None, B=1, T=64, Hq=6, Hkv=2, d=64, rs=None):
+    p = ptrs or [fake(i) for i in range(6)]
+    r = rs or [Hq * d, Hkv * d, Hq * d, Hkv * d]
+    return cg.library().attn_rope_qk(*p, B, T, Hq, Hkv, d, *r, None)
+
+
+def test_rope_rejections():
+    for i in range(6):
+        p = [fake(j) for j in range(6)]
+        p[i] = None
+        assert call_rope(ptrs=p) == cg.CGQA_EINVAL, i
+        p = [fake(j) for j in range(6)]
+        p[i] += 8
+        assert call_rope(ptrs=p) == cg.CGQA_EUNSUPPORTED, i
+    assert call_rope(d=96) == cg.CGQA_EUNSUPPORTED
+    assert call_rope(Hq=6, Hkv=4) == cg.CGQA_EINVAL
+    assert call_rope(rs=[6 * 64 - 8, 128, 384, 128]) == cg.CGQA_EINVAL         # stride shorter than a row
+    assert call_rope(rs=[6 * 64 + 4, 128, 384, 128]) == cg.CGQA_EUNSUPPORTED   # not a multiple of 8
+    # outputs overlapping something other than their own input, at the same place
+    for o in (2, 3):
+        for other in range(6):
+            if other == o:
+                continue
+            p = [fake(j) for j in range(6)]
+            p[o] = p[other] + 64
+            assert call_rope(ptrs=p) == cg.CGQA_EINVAL, (o, other)
+    # in place with a different stride is an overlap
+    p = [fake(j) for j in range(6)]
+    p[2] = p[0]
+    assert call_rope(ptrs=p, rs=[384, 128, 392, 128]) == cg.CGQA_EINVAL
+    assert call_rope(ptrs=[None] * 6, T=0) == cg.CGQA_OK
+
+
+def test_rope_backward_rejections():
+    lib = cg.library()
+    args = (1, 64, 6, 2, 64, 0.125, None)
+    p = [fake(j) for j in range(10)]
+    for fn in (lib.attn_bwd_dq_rope, lib.attn_bwd_dkv_rope):
+        for i in (8, 9):                       # missing table
+            q = list(p)
+            q[i] = None
+            assert fn(*q, *args) == cg.CGQA_EINVAL, i
+        q = list(p)
+        q[8] += 8                               # misaligned table
+        assert fn(*q, *args) == cg.CGQA_EUNSUPPORTED
+        q = list(p)
+        q[8] = q[7] + 64                        # table inside an output
+        assert fn(*q, *args) == cg.CGQA_EINVAL
