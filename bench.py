@@ -166,8 +166,8 @@ def gemm_bench(w, timed, stream):
                                         "unit": "TFLOP/s", "frac": round(best[1] / PEAK_BF16_TFLOPS, 4)},
             "note": "torch_matmul_event_ms: back-to-back torch.matmul (hipBLASLt) on the same bf16 "
                     "operands (bf16 output, no residual), HIP events; at these sizes the Python "
-                    "dispatch of each call can exceed its kernel, so the library's kernel times "
-                    "are read from the rocprofv3 trace instead"}
+                    "dispatch of each call can exceed its kernel, so kernel-only times of both "
+                    "sides come from the rocprofv3 kernel trace"}
 
 
 def cpu_baseline(w, x, budget_s):

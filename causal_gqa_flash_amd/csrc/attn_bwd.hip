@@ -253,6 +253,14 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
         if (hl == 0) a.delta[((size_t)b * Hq + h) * T + query] = dfull;
         const float corr = dfull - dtilde[qb];
         const size_t drow = ((size_t)b * T + query) * a.dq_rs + (size_t)h * D;
+        // Rotary tables of this row, all loaded before the first store.
+        RopeCS rt[C::kMB][4];
+        if (a.rope_cos) {
+#pragma unroll
+            for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) rt[mb][u] = rope_load(a.rope_cos, a.rope_sin, query, D / 2, 32 * mb + 8 * u + 4 * hl);
+        }
 #pragma unroll
         for (int mb = 0; mb < C::kMB; ++mb)
 #pragma unroll
@@ -261,7 +269,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     x[r] = a.scale * fmaf(-corr, kbar[qb][mb][4 * u + r], dqacc[qb][mb][4 * u + r]);
-                if (a.rope_cos) x = rope_back4(x, a.rope_cos, a.rope_sin, query, D / 2, 32 * mb + 8 * u + 4 * hl);
+                if (a.rope_cos) x = rope_back4(x, rt[mb][u]);
                 store_out4(a.dq, drow + 32 * mb + 8 * u + 4 * hl, x, a.grad_bf16);
             }
     }
@@ -608,6 +616,19 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     // 16-byte access of a wave covers 1 KB of consecutive LDS (no bank conflicts).
     float* red = reinterpret_cast<float*>(smem);
     auto red_at = [&](int slot, int u) { return red + (size_t)((((slot - 1) * NKW + pos) * 4 + u) * 64 + lane) * 4; };
+    // Rotary tables of this lane's key (clamped in range for lanes without one), loaded
+    // together before the reduction, by the waves that store, so their latency is paid
+    // once.
+    RopeCS rt[C::kMB][4];
+    if constexpr (ROPE) {
+        if (hs == 0) {   // only head slot 0 stores
+        const int kt_row = min(key, T - 1);
+#pragma unroll
+        for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) rt[mb][u] = rope_load(a.rope_cos, a.rope_sin, kt_row, D / 2, 32 * mb + 8 * u + 4 * hl);
+        }
+    }
     auto reduce_store = [&](f32x16 (&acc)[C::kMB], void* out, float mul, auto Rc) {
         constexpr bool ROT = decltype(Rc)::value;
 #pragma unroll
@@ -643,7 +664,7 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
                     f32x4 x;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) x[r] = acc[mb][4 * u + r] * mul;
-                    if constexpr (ROT) x = rope_back4(x, a.rope_cos, a.rope_sin, key, D / 2, 32 * mb + 8 * u + 4 * hl);
+                    if constexpr (ROT) x = rope_back4(x, rt[mb][u]);
                     store_out4(out, row + 32 * mb + 8 * u + 4 * hl, x, BF16OUT);
                 }
             }
@@ -898,6 +919,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
         if (hl == 0) a.delta[((size_t)b * Hq + h) * T + query] = dfull;
         const float corr = dfull - dtilde;
         const size_t drow = ((size_t)b * T + query) * a.dq_rs + (size_t)h * D;
+        // Rotary tables of this row, all loaded before the first store.
+        RopeCS rt[C::kMB][4];
+        if (a.rope_cos) {
+#pragma unroll
+            for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) rt[mb][u] = rope_load(a.rope_cos, a.rope_sin, query, D / 2, 32 * mb + 8 * u + 4 * hl);
+        }
 #pragma unroll
         for (int mb = 0; mb < C::kMB; ++mb)
 #pragma unroll
@@ -905,7 +934,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
                 f32x4 x;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) x[r] = a.scale * fmaf(-corr, kbar[mb][4 * u + r], dqacc[mb][4 * u + r]);
-                if (a.rope_cos) x = rope_back4(x, a.rope_cos, a.rope_sin, query, D / 2, 32 * mb + 8 * u + 4 * hl);
+                if (a.rope_cos) x = rope_back4(x, rt[mb][u]);
                 store_out4(a.dq, drow + 32 * mb + 8 * u + 4 * hl, x, a.grad_bf16);
             }
     }

@@ -278,20 +278,23 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Rotary embedding, backward: four consecutive dims starting at `dim` (a multiple of 4)
-// of position t hold two pairs (x0, x1), (x2, x3) of a gradient with respect to rotated
-// values; returns the gradient with respect to the unrotated ones, R^T x, using row t of
-// the [T][half_d] cos and sin tables.
-__device__ __forceinline__ f32x4 rope_back4(f32x4 x, const float* cos, const float* sin, size_t t, int half_d,
-                                            int dim) {
-    const size_t i = t * (size_t)half_d + (size_t)(dim / 2);   // even: 8-byte aligned pairs
-    const float2 c = *reinterpret_cast<const float2*>(cos + i), sn = *reinterpret_cast<const float2*>(sin + i);
-    const float c0 = c.x, c1 = c.y, s0 = sn.x, s1 = sn.y;
+// Rotary embedding, backward. The cosines and sines of the two pairs that start at dim
+// `dim` (a multiple of 4) of position t, from [T][half_d] tables (8-byte aligned reads).
+struct RopeCS {
+    float2 c, s;
+};
+__device__ __forceinline__ RopeCS rope_load(const float* cos, const float* sin, size_t t, int half_d, int dim) {
+    const size_t i = t * (size_t)half_d + (size_t)(dim / 2);
+    return {*reinterpret_cast<const float2*>(cos + i), *reinterpret_cast<const float2*>(sin + i)};
+}
+// Four consecutive dims hold two pairs (x0, x1), (x2, x3) of a gradient with respect to
+// rotated values; returns the gradient with respect to the unrotated ones, R^T x.
+__device__ __forceinline__ f32x4 rope_back4(f32x4 x, RopeCS r) {
     f32x4 y;
-    y[0] = fmaf(x[0], c0, x[1] * s0);
-    y[1] = fmaf(x[1], c0, -(x[0] * s0));
-    y[2] = fmaf(x[2], c1, x[3] * s1);
-    y[3] = fmaf(x[3], c1, -(x[2] * s1));
+    y[0] = fmaf(x[0], r.c.x, x[1] * r.s.x);
+    y[1] = fmaf(x[1], r.c.x, -(x[0] * r.s.x));
+    y[2] = fmaf(x[2], r.c.y, x[3] * r.s.y);
+    y[3] = fmaf(x[3], r.c.y, -(x[2] * r.s.y));
     return y;
 }
 
