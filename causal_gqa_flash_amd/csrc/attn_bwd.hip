@@ -56,17 +56,35 @@ struct DqCfg {
     static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
+// Query tile and (batch, head) of dQ workgroup bid, heaviest query tiles first. Workgroup
+// x runs on XCD x mod 8; when the (batch, kv head) slices split evenly over the eight XCDs,
+// every head and tile of a slice goes to the slice's XCD, whose L2 then serves its K and V
+// to all heads of the group (otherwise the group's heads land on different XCDs and each
+// fetches the slice's K and V from HBM).
+struct DqTile { int qt, b, h; };
+__device__ inline DqTile dq_tile(const BwdArgs& a, int bid) {
+    const int G = a.Hq / a.Hkv;
+    if (a.xcd_group) {
+        const int xcd = bid & 7;
+        const int per_qt = ((a.B * a.Hkv) >> 3) * G;   // workgroups per query tile on one XCD
+        const int local = bid >> 3;
+        const int rem = local % per_qt;
+        const int p = xcd + 8 * (rem / G);               // slice b * Hkv + g
+        return {a.n_tiles - 1 - local / per_qt, p / a.Hkv, (p % a.Hkv) * G + rem % G};
+    }
+    const int bh_count = a.B * a.Hq;
+    const int bh = bid % bh_count;
+    return {a.n_tiles - 1 - bid / bh_count, bh / a.Hq, bh % a.Hq};
+}
+
 template <int D, int NQB, int BN, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     using C = DqCfg<D, NQB, BN, NW>;
     __shared__ __attribute__((aligned(16))) char smem[C::kLds];
 
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
-    const int bh_count = a.B * Hq;
-    const int bid = blockIdx.x;
-    const int qt = a.n_tiles - 1 - bid / bh_count;
-    const int bh = bid % bh_count;
-    const int b = bh / Hq, h = bh % Hq;
+    const DqTile wg = dq_tile(a, blockIdx.x);
+    const int qt = wg.qt, b = wg.b, h = wg.h;
     const int g = h / (Hq / Hkv);
 
     const int tid = threadIdx.x;
@@ -715,12 +733,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
     // Workgroup-uniform indices (readfirstlane keeps the integer divisions' results,
     // and everything derived from them, in scalar registers).
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
-    const int bh_count = a.B * Hq;
-    const int bid = blockIdx.x;
-    const int qt = __builtin_amdgcn_readfirstlane(a.n_tiles - 1 - bid / bh_count);   // heaviest first
-    const int bh = __builtin_amdgcn_readfirstlane(bid % bh_count);
-    const int b = __builtin_amdgcn_readfirstlane(bh / Hq);
-    const int h = __builtin_amdgcn_readfirstlane(bh % Hq);
+    const DqTile wg = dq_tile(a, blockIdx.x);
+    const int qt = __builtin_amdgcn_readfirstlane(wg.qt);   // heaviest first
+    const int b = __builtin_amdgcn_readfirstlane(wg.b);
+    const int h = __builtin_amdgcn_readfirstlane(wg.h);
     const int g = __builtin_amdgcn_readfirstlane(h / (Hq / Hkv));
 
     const int tid = threadIdx.x;
@@ -945,6 +961,7 @@ static hipError_t launch_dq_pipe(const BwdArgs& a, hipStream_t stream) {
     using C = DqPipeCfg<D>;
     BwdArgs x = a;
     x.n_tiles = (a.T + C::kBM - 1) / C::kBM;
+    x.xcd_group = (a.B * a.Hkv) % 8 == 0 ? 1 : 0;
     const long blocks = (long)x.n_tiles * a.B * a.Hq;
     hipLaunchKernelGGL((attn_bwd_dq_pipe_kernel<D>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, x);
     return hipGetLastError();
@@ -955,6 +972,7 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream) {
     using C = DqCfg<D, NQB, BN, NW>;
     BwdArgs x = a;
     x.n_tiles = (a.T + C::kBM - 1) / C::kBM;
+    x.xcd_group = (a.B * a.Hkv) % 8 == 0 ? 1 : 0;
     const long blocks = (long)x.n_tiles * a.B * a.Hq;
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, NQB, BN, NW>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
                        stream, x);

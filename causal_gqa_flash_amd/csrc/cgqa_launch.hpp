@@ -45,6 +45,7 @@ struct BwdArgs {
     float scale_log2;   // scale * log2(e)
     int n_tiles;        // set by the launcher
     int zigzag;         // dK/dV: deal key blocks in zig-zag order (set by the launcher)
+    int xcd_group;      // dQ: keep each (batch, kv head) slice on one XCD (set by the launcher)
 };
 
 // Naive attention (attn_naive.hip): contiguous tensors, fp32 workspace p of B*Hq*T*T
