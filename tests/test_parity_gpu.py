@@ -37,6 +37,11 @@ SMALL = [
     (1, 96, 6, 1, 64, 15, 2.0),
     (1, 130, 8, 1, 64, 16, 1.0),
     (2, 77, 6, 2, 128, 17, 1.0),
+    # B * Hkv divisible by 8 (the dQ and forward workgroups of one (batch, kv head) slice
+    # grouped on one XCD) with ragged tails
+    (4, 150, 6, 2, 64, 18, 1.0),
+    (8, 45, 4, 2, 64, 19, 2.0),
+    (2, 333, 12, 4, 64, 20, 1.0),
 ]
 
 
