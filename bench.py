@@ -123,11 +123,13 @@ def pmc_summarize(fetch_dir, write_dir, out_path):
     print(json.dumps(out), flush=True)
 
 
-def gemm_bench(w, timed, stream):
+def gemm_bench(w, graph_timed):
     """The projections around attention for the workload's B*T tokens (model width Hq*d,
     fused QKV width (Hq + 2 Hkv) d): forward QKV and WO (+ residual), and the QKV
     projection's dX and dW, each timed through cgqa_gemm, with torch.matmul (hipBLASLt)
-    on the same bf16 operands beside it for reference."""
+    on the same bf16 operands beside it for reference. Both sides are timed as replays of
+    a captured HIP graph of back-to-back calls (their host dispatch exceeds these short
+    kernels) on the current stream."""
     import torch
     import causal_gqa_flash_amd as cg
     g = torch.Generator(device="cuda")
@@ -141,33 +143,32 @@ def gemm_bench(w, timed, stream):
     c_dw = torch.empty(Q, D, device="cuda")
     ws_dw = torch.empty((max(cg.gemm_workspace_bytes(Q, D, Mt), 4) // 4,), device="cuda")
     cases = {
-        "qkv": (Mt, Q, D, lambda: cg.gemm(x, wqkv, c=c_qkv, stream=stream),
+        "qkv": (Mt, Q, D, lambda: cg.gemm(x, wqkv, c=c_qkv),
                 lambda: torch.matmul(x, wqkv.t())),
-        "wo_residual": (Mt, D, D, lambda: cg.gemm(x, wo, r=resid, c=c_f32, stream=stream),
+        "wo_residual": (Mt, D, D, lambda: cg.gemm(x, wo, r=resid, c=c_f32),
                         lambda: torch.matmul(x, wo.t())),
-        "dx_qkv": (Mt, D, Q, lambda: cg.gemm(dqkv, wqkv, c=c_f32, b_kn=True, stream=stream),
+        "dx_qkv": (Mt, D, Q, lambda: cg.gemm(dqkv, wqkv, c=c_f32, b_kn=True),
                    lambda: torch.matmul(dqkv, wqkv)),
-        "dw_qkv": (Q, D, Mt, lambda: cg.gemm(dqkv, x, c=c_dw, a_km=True, b_kn=True, workspace=ws_dw,
-                                             stream=stream),
+        "dw_qkv": (Q, D, Mt, lambda: cg.gemm(dqkv, x, c=c_dw, a_km=True, b_kn=True, workspace=ws_dw),
                    lambda: torch.matmul(dqkv.t(), x)),
     }
     res, best = {}, None
     for name, (M, N, K, ours, lib) in cases.items():
         ours(); lib()
         torch.cuda.synchronize()
-        ms, ms_lib = timed(ours, 20), timed(lib, 20)
+        ms, ms_lib = graph_timed(ours, 20), graph_timed(lib, 20)
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
         res[name] = {"M": M, "N": N, "K": K, "ms": round(ms, 5), "tflops": round(tf, 1),
-                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "torch_matmul_event_ms": round(ms_lib, 5)}
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "torch_matmul_ms": round(ms_lib, 5)}
         if best is None or tf > best[1]:
             best = (name, tf)
     return {"shapes": res, "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (" + best[0] + ")",
                                         "achieved": round(best[1], 1), "peak": PEAK_BF16_TFLOPS,
                                         "unit": "TFLOP/s", "frac": round(best[1] / PEAK_BF16_TFLOPS, 4)},
-            "note": "torch_matmul_event_ms: back-to-back torch.matmul (hipBLASLt) on the same bf16 "
-                    "operands (bf16 output, no residual), HIP events; at these sizes the Python "
-                    "dispatch of each call can exceed its kernel, so kernel-only times of both "
-                    "sides come from the rocprofv3 kernel trace"}
+            "note": "ms: one call's share of a replayed HIP graph of 20 back-to-back calls "
+                    "(HIP events, median of repeats); torch_matmul_ms: the same for torch.matmul "
+                    "(hipBLASLt) on the same bf16 operands (bf16 output, no residual)"}
 
 
 def cpu_baseline(w, x, budget_s):
@@ -273,6 +274,44 @@ def main():
             per.append(e0.elapsed_time(e1) / n)
         return float(np.median(per))
 
+    graph_failures = []
+
+    def graph_timed(fn, n):
+        """As timed, for kernels shorter than their host dispatch: the n calls are captured
+        once in a HIP graph (fn launches on the current stream) and the graph is replayed.
+        If the capture fails, falls back to timed and records the failure."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):   # warm-up off the default stream, as capture wants
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        try:
+            with torch.cuda.graph(graph):
+                for _ in range(n):
+                    fn()
+        except RuntimeError as e:
+            print(f"graph capture failed: {e}", file=sys.stderr, flush=True)
+            graph_failures.append(getattr(fn, "__name__", "call"))
+            torch.cuda.synchronize()
+            return timed(fn, n)
+        torch.cuda.synchronize()
+        graph.replay()
+        cur = torch.cuda.current_stream()
+        per = []
+        for _ in range(args.repeats):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(cur)
+            graph.replay()
+            e1.record(cur)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / n)
+        del graph
+        return float(np.median(per))
+
     # Clock settle: untimed steps until settle_ms of wall time has passed, then the W
     # warmup steps. Both run the full step; neither is inside the timed region.
     settle_steps = 0
@@ -353,7 +392,7 @@ def main():
                         "flash_speedup_bwd": round(nb / bwd_ms, 1)}
         del ws
     if not args.no_gemm:
-        out["gemm"] = gemm_bench(w, timed, stream)
+        out["gemm"] = gemm_bench(w, graph_timed)
     if not args.no_rope:
         # Rotary embedding: the rotation pass of Q and K (HBM-bound: each element read and
         # written once, plus the tables), and the backward with dQ, dK turned back inside.
@@ -362,19 +401,21 @@ def main():
         q_rot = torch.empty_like(q)
         k_rot = torch.empty_like(k)
         def rope_pass():
-            cg.rope_qk(q, k, rc, rs, q_out=q_rot, k_out=k_rot, stream=stream)
+            cg.rope_qk(q, k, rc, rs, q_out=q_rot, k_out=k_rot)
         def bwd_rope():
             cg.attn_bwd_dq(q, k, v, o, do, lse, scale=w.scale, delta=delta, dq=dq, stream=stream, rope=(rc, rs))
             cg.attn_bwd_dkv(q, k, v, do, lse, delta, scale=w.scale, dk=dk, dv=dv, stream=stream, rope=(rc, rs))
         rope_pass(); bwd_rope()
         torch.cuda.synchronize()
-        ms_rope, ms_bwd_rope = timed(rope_pass, args.steps), timed(bwd_rope, args.steps)
+        ms_rope, ms_bwd_rope = graph_timed(rope_pass, args.steps), timed(bwd_rope, args.steps)
         rope_bytes = 2 * 2 * w.B * w.T * (w.Hq + w.Hkv) * w.d + 2 * 4 * w.T * (w.d // 2)
         gbs = rope_bytes / (ms_rope * 1e-3) / 1e9
         out["rope"] = {"pass_ms": round(ms_rope, 5), "bytes": rope_bytes,
                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)},
                        "bwd_ms": round(ms_bwd_rope, 5), "bwd_plain_ms": round(bwd_ms, 5)}
+    if graph_failures:
+        out["graph_capture_failed"] = graph_failures   # these were timed call by call instead
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
