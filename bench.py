@@ -27,11 +27,12 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 dense bf16/fp16 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "B16_T1024_Hq6_Hkv2_d64"
-KERNEL_SOURCES = ["causal_gqa_flash_amd/csrc/attn_fwd.hip", "causal_gqa_flash_amd/csrc/attn_bwd.hip",
+KERNEL_SOURCES = ["causal_gqa_flash_amd/csrc/attn_fwd.hip", "causal_gqa_flash_amd/csrc/attn_fwd_par.hip",
+                  "causal_gqa_flash_amd/csrc/attn_bwd.hip",
                   "causal_gqa_flash_amd/csrc/cgqa_device.hpp", "causal_gqa_flash_amd/csrc/cgqa_launch.hpp",
                   "causal_gqa_flash_amd/csrc/api.hip", "causal_gqa_flash_amd/build.py"]
 # Device kernels behind each entry point (the one a launch uses depends on d and the shape).
-KERNEL_NAMES = {"attn_fwd": ("attn_fwd_kernel", "attn_fwd_split_kernel"),
+KERNEL_NAMES = {"attn_fwd": ("attn_fwd_kernel", "attn_fwd_par_kernel"),
                 "attn_bwd_dq": ("attn_bwd_dq_kernel", "attn_bwd_dq_pipe_kernel"),
                 "attn_bwd_dkv": ("attn_bwd_dkv_kernel",)}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_B16_T1024_Hq6_Hkv2_d64.json")

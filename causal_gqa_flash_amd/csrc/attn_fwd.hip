@@ -43,9 +43,6 @@
 #include "cgqa_device.hpp"
 #include "cgqa_launch.hpp"
 
-#include <stdlib.h>
-#include <string.h>
-
 #include <type_traits>
 
 namespace cgqa {
@@ -455,12 +452,10 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Forward kernel choice: the tiled kernel above. The balanced kernel
-// (attn_fwd_split.hip) is parity-tested but slower on every measured workload, so it
-// runs only when CGQA_FWD_KERNEL=split asks for it on a shape it supports.
+// Forward kernel choice, by shape alone: d = 64 grids too small to fill the chip go to the
+// key-split kernel (attn_fwd_par.hip), every other shape to the tiled kernel above.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-    const char* force = getenv("CGQA_FWD_KERNEL");
-    if (force && strcmp(force, "split") == 0 && fwd_split_supported(a)) return launch_fwd_split(a, stream);
+    if (fwd_split_keys_chosen(a)) return launch_fwd_split_keys(a, stream);
     if (a.d == 64) return launch_fwd_t<64>(a, stream);
     return launch_fwd_t<128>(a, stream);
 }

@@ -99,10 +99,10 @@ struct RopeArgs {
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
-// Balanced forward for d = 64 and whole 64-query blocks (attn_fwd_split.hip).
-bool fwd_split_supported(const FwdArgs& a);
-long fwd_split_blocks(const FwdArgs& a);
-hipError_t launch_fwd_split(const FwdArgs& a, hipStream_t stream);
+// Forward with every query block's keys split over two waves (attn_fwd_par.hip), for
+// d = 64 grids that would not fill the chip with the tiled kernel.
+bool fwd_split_keys_chosen(const FwdArgs& a);
+hipError_t launch_fwd_split_keys(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_naive_fwd(const NaiveArgs& a, hipStream_t stream);

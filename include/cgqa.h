@@ -227,7 +227,10 @@ int cgqa_gemm(const uint16_t* A, const uint16_t* B, void* C, const float* R,
               int M, int N, int K, int flags, float* workspace, size_t workspace_bytes,
               void* stream);
 
-/* Static description of a return code (never NULL). */
+/* Static description of a return code (never NULL): every call reports failure as a code
+ * whose meaning can be printed, the library-side form of the pages' practice of naming each
+ * failed call and the error behind it (page "Talking to the GPU", section "One macro for
+ * every call"; a library returns the code instead of exiting). */
 const char* attn_status_string(int status);
 
 /* The HIP error code behind the calling thread's last CGQA_EHIP (0 if none). */

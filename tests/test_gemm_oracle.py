@@ -84,3 +84,16 @@ def test_round_to_bf16_matches_torch_cast():
     want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
     got = og.round_to_bf16(x.astype(np.float32).astype(np.float64))
     assert np.array_equal(got, want)
+
+
+def test_abs_product_worked_example():
+    # |A| |B|^T by hand for A = [[1, -2], [-3, 4]], B (stored [N][K]) = [[-1, 2], [0.5, -0.25]]:
+    # row 0: |1|*|-1| + |-2|*|2| = 5, |1|*0.5 + |-2|*0.25 = 1; row 1: 3 + 8 = 11, 1.5 + 1 = 2.5.
+    # (A plain product would give [[-5, 1], [11, -2.5]]: a dropped absolute value changes
+    # the signs, a dropped term the sizes.)
+    a = bits([[1, -2], [-3, 4]])
+    b = bits([[-1, 2], [0.5, -0.25]])
+    assert og.abs_product(a, b).tolist() == [[5.0, 1.0], [11.0, 2.5]]
+    # stored the other way round: the same bound
+    assert og.abs_product(bits(np.array([[1, -2], [-3, 4]]).T), b, a_km=True).tolist() == [[5.0, 1.0], [11.0, 2.5]]
+    assert og.abs_product(a, bits(np.array([[-1, 2], [0.5, -0.25]]).T), b_kn=True).tolist() == [[5.0, 1.0], [11.0, 2.5]]

