@@ -239,7 +239,7 @@ def main():
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device="cuda")
-    delta = torch.empty_like(lse)
+    delta = cg.bwd_delta(w.B, w.Hq, w.T, device="cuda")
     dq = torch.empty((w.B, w.T, w.Hq, w.d), dtype=torch.float32, device="cuda")
     dk = torch.empty((w.B, w.T, w.Hkv, w.d), dtype=torch.float32, device="cuda")
     dv = torch.empty_like(dk)

@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     attn_naive_fwd,
     attn_naive_workspace_bytes,
     attn_status_string,
+    bwd_delta,
     gemm,
     gemm_workspace_bytes,
     library,

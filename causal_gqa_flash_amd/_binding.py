@@ -44,15 +44,15 @@ def library():
         f = ctypes.c_float
         lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.attn_fwd.restype = i
-        lib.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.attn_bwd_dq.restype = i
-        lib.attn_bwd_dkv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.attn_bwd_dkv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.attn_bwd_dkv.restype = i
         lib.attn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
         lib.attn_fwd_strided.restype = i
-        lib.attn_bwd_dq_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i, f, vp]
+        lib.attn_bwd_dq_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i, f, vp]
         lib.attn_bwd_dq_strided.restype = i
-        lib.attn_bwd_dkv_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, vp]
+        lib.attn_bwd_dkv_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, vp]
         lib.attn_bwd_dkv_strided.restype = i
         sz = ctypes.c_size_t
         lib.attn_naive_workspace_bytes.argtypes = [i, i, i]
@@ -64,9 +64,9 @@ def library():
         lib.cgqa_gemm.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, ctypes.c_size_t, vp]
         lib.attn_rope_qk.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp]
         lib.attn_rope_qk.restype = i
-        lib.attn_bwd_dq_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.attn_bwd_dq_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.attn_bwd_dq_rope.restype = i
-        lib.attn_bwd_dkv_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.attn_bwd_dkv_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.attn_bwd_dkv_rope.restype = i
         lib.cgqa_gemm_workspace_bytes.argtypes = [i, i, i]
         lib.cgqa_gemm_workspace_bytes.restype = ctypes.c_size_t
@@ -187,9 +187,36 @@ def _rope_tables(rope, T, d):
     return cos, sin
 
 
+def _absmax_layout(B, Hq, T):
+    """(offset, count) in floats of the dO block maxima behind a delta of B*Hq*T floats
+    (offset rounded up to 16 bytes)."""
+    n = B * Hq * T
+    return (n + 3) // 4 * 4, B * Hq * ((T + 31) // 32)
+
+
+def bwd_delta(B, Hq, T, device=None):
+    """The delta that attn_bwd_dq writes and attn_bwd_dkv reads: a [B, Hq, T] fp32 view at
+    the start of an allocation that also holds the dO block maxima (B*Hq*ceil(T/32)
+    floats, the dO_absmax workspace of the C calls) that carry the scale of dO from one
+    call to the other."""
+    torch = _torch()
+    off, nm = _absmax_layout(B, Hq, T)
+    buf = torch.empty(off + nm, dtype=torch.float32, device=device)
+    return buf[:B * Hq * T].view(B, Hq, T)
+
+
+def _absmax_ptr(delta, B, Hq, T):
+    off, nm = _absmax_layout(B, Hq, T)
+    if (delta.storage_offset() + off + nm) * 4 > delta.untyped_storage().nbytes():
+        raise ValueError("delta must come from bwd_delta() or attn_bwd_dq (its allocation carries the dO maxima)")
+    return ctypes.c_void_p(delta.data_ptr() + 4 * off)
+
+
 def attn_bwd_dq(q, k, v, o, do, lse, scale=None, delta=None, dq=None, stream=None, grad_dtype=None, rope=None):
     """delta [B,Hq,T] fp32 and dq [B,T,Hq,d], fp32 or bf16 (the dtype of the dq given,
-    else grad_dtype, else fp32). Inputs and dq may be row-strided views. With
+    else grad_dtype, else fp32). delta, if given, comes from bwd_delta(): its allocation
+    also receives the dO block maxima for attn_bwd_dkv. Inputs and dq may be row-strided
+    views. With
     rope=(cos, sin) (fp32 [T, d/2]), q and k are the rotated tensors and dq is returned
     with respect to the unrotated q (contiguous tensors, fp32 dq)."""
     torch = _torch()
@@ -200,10 +227,11 @@ def attn_bwd_dq(q, k, v, o, do, lse, scale=None, delta=None, dq=None, stream=Non
                      _need(v, "v", torch.bfloat16, (B, T, Hkv, d), rows=True))
     _need(lse, "lse", torch.float32, (B, Hq, T))
     if delta is None:
-        delta = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+        delta = bwd_delta(B, Hq, T, device=q.device)
     if dq is None:
         dq = torch.empty((B, T, Hq, d), dtype=grad_dtype or torch.float32, device=q.device)
     _need(delta, "delta", torch.float32, (B, Hq, T))
+    am = _absmax_ptr(delta, B, Hq, T)
     rdq = _need(dq, "dq", (torch.float32, torch.bfloat16), (B, T, Hq, d), rows=True)
     lib = library()
     contiguous = (rq, rkv, ro, rdo, rdq) == (Hq * d, Hkv * d, Hq * d, Hq * d, Hq * d)
@@ -212,22 +240,23 @@ def attn_bwd_dq(q, k, v, o, do, lse, scale=None, delta=None, dq=None, stream=Non
             raise ValueError("the rotary backward takes contiguous tensors and an fp32 dq")
         cos, sin = _rope_tables(rope, T, d)
         _check("attn_bwd_dq_rope", lib.attn_bwd_dq_rope(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(cos), _ptr(sin),
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(delta), am, _ptr(dq), _ptr(cos), _ptr(sin),
             B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
     elif contiguous and dq.dtype == torch.float32:
         _check("attn_bwd_dq", lib.attn_bwd_dq(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq),
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(delta), am, _ptr(dq),
             B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
     else:
         _check("attn_bwd_dq_strided", lib.attn_bwd_dq_strided(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq),
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(delta), am, _ptr(dq),
             B, T, Hq, Hkv, d, rq, rkv, ro, rdo, rdq, _grad_code(dq.dtype), _scale(scale, d), _stream_ptr(stream)))
     return delta, dq
 
 
 def attn_bwd_dkv(q, k, v, do, lse, delta, scale=None, dk=None, dv=None, stream=None, grad_dtype=None, rope=None):
     """dk, dv [B,T,Hkv,d], fp32 or bf16 (the dtype of the dk/dv given, else grad_dtype,
-    else fp32). Enqueue after attn_bwd_dq on the same stream. Inputs and dk, dv may be
+    else fp32). Enqueue after attn_bwd_dq on the same stream, with the delta it returned
+    (whose allocation carries the dO maxima). Inputs and dk, dv may be
     row-strided views (dk and dv with one row stride). With rope=(cos, sin), q and k are
     the rotated tensors and dk is returned with respect to the unrotated k (contiguous
     tensors, fp32 gradients)."""
@@ -238,6 +267,7 @@ def attn_bwd_dkv(q, k, v, do, lse, delta, scale=None, dk=None, dv=None, stream=N
                      _need(v, "v", torch.bfloat16, (B, T, Hkv, d), rows=True))
     _need(lse, "lse", torch.float32, (B, Hq, T))
     _need(delta, "delta", torch.float32, (B, Hq, T))
+    am = _absmax_ptr(delta, B, Hq, T)
     if dk is None:
         dk = torch.empty((B, T, Hkv, d), dtype=grad_dtype or torch.float32, device=q.device)
     if dv is None:
@@ -255,15 +285,15 @@ def attn_bwd_dkv(q, k, v, do, lse, delta, scale=None, dk=None, dv=None, stream=N
             raise ValueError("the rotary backward takes contiguous tensors and fp32 dk, dv")
         cos, sin = _rope_tables(rope, T, d)
         _check("attn_bwd_dkv_rope", lib.attn_bwd_dkv_rope(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv), _ptr(cos), _ptr(sin),
+            _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), am, _ptr(dk), _ptr(dv), _ptr(cos), _ptr(sin),
             B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
     elif contiguous and dk.dtype == torch.float32:
         _check("attn_bwd_dkv", lib.attn_bwd_dkv(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
+            _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), am, _ptr(dk), _ptr(dv),
             B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
     else:
         _check("attn_bwd_dkv_strided", lib.attn_bwd_dkv_strided(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
+            _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), am, _ptr(dk), _ptr(dv),
             B, T, Hq, Hkv, d, rq, rkv, rdo, rdk, _grad_code(dk.dtype), _scale(scale, d), _stream_ptr(stream)))
     return dk, dv
 

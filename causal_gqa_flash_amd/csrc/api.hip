@@ -103,7 +103,7 @@ struct BwdStrides {
 
 int bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
              const uint16_t* dO, const float* lse, const float* delta_in, float* delta_out,
-             void* dq, void* dk, void* dv, int B, int T, int Hq, int Hkv, int d, const BwdStrides& st,
+             const float* absmax_in, float* absmax_out, void* dq, void* dk, void* dv, int B, int T, int Hq, int Hkv, int d, const BwdStrides& st,
              float scale, void* stream, bool is_dq, const float* rope_cos = nullptr,
              const float* rope_sin = nullptr) {
     bool empty = false;
@@ -111,6 +111,7 @@ int bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
     if (rc != CGQA_OK) return rc;
     if (st.grad != CGQA_GRAD_F32 && st.grad != CGQA_GRAD_BF16) return CGQA_EINVAL;
     const int64_t rows = (int64_t)B * T, wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d, nr = (int64_t)B * Hq * T;
+    const int64_t nm = (int64_t)B * Hq * ((T + 31) / 32);   // dO block maxima
     const int64_t geb = st.grad == CGQA_GRAD_BF16 ? 2 : 4;
     int64_t rcs[4] = {check_stride(st.q_rs, wq, rows, 8), check_stride(st.kv_rs, wkv, rows, 8),
                       check_stride(st.do_rs, wq, rows, 8),
@@ -126,22 +127,26 @@ int bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
     const View vq{q, rows, wq, st.q_rs, 2}, vk{k, rows, wkv, st.kv_rs, 2}, vv{v, rows, wkv, st.kv_rs, 2},
         vdo{dO, rows, wq, st.do_rs, 2}, vl{lse, 1, nr, nr, 4};
     if (is_dq) {
-        if (!q || !k || !v || !o || !dO || !lse || !delta_out || !dq) return CGQA_EINVAL;
+        if (!q || !k || !v || !o || !dO || !lse || !delta_out || !absmax_out || !dq) return CGQA_EINVAL;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
-            !aligned16(lse) || !aligned16(delta_out) || !aligned16(dq))
+            !aligned16(lse) || !aligned16(delta_out) || !aligned16(absmax_out) || !aligned16(dq))
             return CGQA_EUNSUPPORTED;
-        const View outs[2] = {View{delta_out, 1, nr, nr, 4}, View{dq, rows, wq, st.dq_rs, geb}};
+        const View outs[3] = {View{delta_out, 1, nr, nr, 4}, View{dq, rows, wq, st.dq_rs, geb},
+                              View{absmax_out, 1, nm, nm, 4}};
         const View ins[6] = {vq, vk, vv, View{o, rows, wq, st.o_rs, 2}, vdo, vl};
-        if (!disjoint(outs[0], outs[1])) return CGQA_EINVAL;
+        for (int x = 0; x < 3; ++x)
+            for (int y = x + 1; y < 3; ++y)
+                if (!disjoint(outs[x], outs[y])) return CGQA_EINVAL;
         for (const View& s : ins)
-            if (!disjoint(s, outs[0]) || !disjoint(s, outs[1])) return CGQA_EINVAL;
+            for (const View& t : outs)
+                if (!disjoint(s, t)) return CGQA_EINVAL;
     } else {
-        if (!q || !k || !v || !dO || !lse || !delta_in || !dk || !dv) return CGQA_EINVAL;
+        if (!q || !k || !v || !dO || !lse || !delta_in || !absmax_in || !dk || !dv) return CGQA_EINVAL;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) ||
-            !aligned16(delta_in) || !aligned16(dk) || !aligned16(dv))
+            !aligned16(delta_in) || !aligned16(absmax_in) || !aligned16(dk) || !aligned16(dv))
             return CGQA_EUNSUPPORTED;
         const View outs[2] = {View{dk, rows, wkv, st.dkv_rs, geb}, View{dv, rows, wkv, st.dkv_rs, geb}};
-        const View ins[6] = {vq, vk, vv, vdo, vl, View{delta_in, 1, nr, nr, 4}};
+        const View ins[7] = {vq, vk, vv, vdo, vl, View{delta_in, 1, nr, nr, 4}, View{absmax_in, 1, nm, nm, 4}};
         if (!disjoint(outs[0], outs[1])) return CGQA_EINVAL;
         for (const View& s : ins)
             if (!disjoint(s, outs[0]) || !disjoint(s, outs[1])) return CGQA_EINVAL;
@@ -153,14 +158,15 @@ int bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
         const View vc{rope_cos, 1, nt, nt, 4}, vs{rope_sin, 1, nt, nt, 4};
         const View outs[3] = {is_dq ? View{delta_out, 1, nr, nr, 4} : View{dk, rows, wkv, st.dkv_rs, geb},
                               is_dq ? View{dq, rows, wq, st.dq_rs, geb} : View{dv, rows, wkv, st.dkv_rs, geb},
-                              vc};
-        for (int x = 0; x < 2; ++x)
+                              is_dq ? View{absmax_out, 1, nm, nm, 4} : View{dv, rows, wkv, st.dkv_rs, geb}};
+        for (int x = 0; x < 3; ++x)
             if (!disjoint(outs[x], vc) || !disjoint(outs[x], vs)) return CGQA_EINVAL;
     }
     cgqa::BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
     a.rope_cos = rope_cos; a.rope_sin = rope_sin;
     a.delta = is_dq ? delta_out : const_cast<float*>(delta_in);
+    a.do_absmax = is_dq ? absmax_out : const_cast<float*>(absmax_in);
     a.dq = dq; a.dk = dk; a.dv = dv;
     a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
     a.q_rs = st.q_rs; a.kv_rs = st.kv_rs; a.o_rs = st.o_rs; a.do_rs = st.do_rs;
@@ -300,24 +306,26 @@ int attn_rope_qk(const uint16_t* q, const uint16_t* k, uint16_t* q_out, uint16_t
 }
 
 int attn_bwd_dq_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
-                     const uint16_t* dO, const float* lse, float* delta, float* dq, const float* rope_cos,
+                     const uint16_t* dO, const float* lse, float* delta, float* dO_absmax, float* dq,
+                     const float* rope_cos,
                      const float* rope_sin, int B, int T, int Hq, int Hkv, int d, float scale, void* stream) {
     const int64_t wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d;
     if (Hq < 1 || Hkv < 1 || wq >= ((int64_t)1 << 31)) return CGQA_EINVAL;
     if (!rope_cos || !rope_sin) return CGQA_EINVAL;
     const BwdStrides st{(int)wq, (int)wkv, (int)wq, (int)wq, (int)wq, (int)wkv, CGQA_GRAD_F32};
-    return bwd_impl(q, k, v, o, dO, lse, nullptr, delta, dq, nullptr, nullptr, B, T, Hq, Hkv, d, st, scale,
+    return bwd_impl(q, k, v, o, dO, lse, nullptr, delta, nullptr, dO_absmax, dq, nullptr, nullptr, B, T, Hq, Hkv, d, st, scale,
                     stream, true, rope_cos, rope_sin);
 }
 
 int attn_bwd_dkv_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
-                      const float* lse, const float* delta, float* dk, float* dv, const float* rope_cos,
+                      const float* lse, const float* delta, const float* dO_absmax, float* dk, float* dv,
+                      const float* rope_cos,
                       const float* rope_sin, int B, int T, int Hq, int Hkv, int d, float scale, void* stream) {
     const int64_t wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d;
     if (Hq < 1 || Hkv < 1 || wq >= ((int64_t)1 << 31)) return CGQA_EINVAL;
     if (!rope_cos || !rope_sin) return CGQA_EINVAL;
     const BwdStrides st{(int)wq, (int)wkv, (int)wq, (int)wq, (int)wq, (int)wkv, CGQA_GRAD_F32};
-    return bwd_impl(q, k, v, nullptr, dO, lse, delta, nullptr, nullptr, dk, dv, B, T, Hq, Hkv, d, st, scale,
+    return bwd_impl(q, k, v, nullptr, dO, lse, delta, nullptr, dO_absmax, nullptr, nullptr, dk, dv, B, T, Hq, Hkv, d, st, scale,
                     stream, false, rope_cos, rope_sin);
 }
 
@@ -366,41 +374,41 @@ int attn_fwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, ui
 }
 
 int attn_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
-                const uint16_t* dO, const float* lse, float* delta, float* dq,
+                const uint16_t* dO, const float* lse, float* delta, float* dO_absmax, float* dq,
                 int B, int T, int Hq, int Hkv, int d, float scale, void* stream) {
     const int64_t wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d;
     if (Hq < 1 || Hkv < 1 || wq >= ((int64_t)1 << 31)) return CGQA_EINVAL;
     const BwdStrides st{(int)wq, (int)wkv, (int)wq, (int)wq, (int)wq, (int)wkv, CGQA_GRAD_F32};
-    return bwd_impl(q, k, v, o, dO, lse, nullptr, delta, dq, nullptr, nullptr, B, T, Hq, Hkv, d, st, scale,
+    return bwd_impl(q, k, v, o, dO, lse, nullptr, delta, nullptr, dO_absmax, dq, nullptr, nullptr, B, T, Hq, Hkv, d, st, scale,
                     stream, true);
 }
 
 int attn_bwd_dkv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
-                 const float* lse, const float* delta, float* dk, float* dv,
+                 const float* lse, const float* delta, const float* dO_absmax, float* dk, float* dv,
                  int B, int T, int Hq, int Hkv, int d, float scale, void* stream) {
     const int64_t wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d;
     if (Hq < 1 || Hkv < 1 || wq >= ((int64_t)1 << 31)) return CGQA_EINVAL;
     const BwdStrides st{(int)wq, (int)wkv, (int)wq, (int)wq, (int)wq, (int)wkv, CGQA_GRAD_F32};
-    return bwd_impl(q, k, v, nullptr, dO, lse, delta, nullptr, nullptr, dk, dv, B, T, Hq, Hkv, d, st, scale,
+    return bwd_impl(q, k, v, nullptr, dO, lse, delta, nullptr, dO_absmax, nullptr, nullptr, dk, dv, B, T, Hq, Hkv, d, st, scale,
                     stream, false);
 }
 
 int attn_bwd_dq_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
-                        const uint16_t* dO, const float* lse, float* delta, void* dq,
+                        const uint16_t* dO, const float* lse, float* delta, float* dO_absmax, void* dq,
                         int B, int T, int Hq, int Hkv, int d, int q_row_stride, int kv_row_stride,
                         int o_row_stride, int do_row_stride, int dq_row_stride, int grad_dtype,
                         float scale, void* stream) {
     const BwdStrides st{q_row_stride, kv_row_stride, o_row_stride, do_row_stride, dq_row_stride, 0, grad_dtype};
-    return bwd_impl(q, k, v, o, dO, lse, nullptr, delta, dq, nullptr, nullptr, B, T, Hq, Hkv, d, st, scale,
+    return bwd_impl(q, k, v, o, dO, lse, nullptr, delta, nullptr, dO_absmax, dq, nullptr, nullptr, B, T, Hq, Hkv, d, st, scale,
                     stream, true);
 }
 
 int attn_bwd_dkv_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
-                         const float* lse, const float* delta, void* dk, void* dv,
+                         const float* lse, const float* delta, const float* dO_absmax, void* dk, void* dv,
                          int B, int T, int Hq, int Hkv, int d, int q_row_stride, int kv_row_stride,
                          int do_row_stride, int dkv_row_stride, int grad_dtype, float scale, void* stream) {
     const BwdStrides st{q_row_stride, kv_row_stride, 0, do_row_stride, 0, dkv_row_stride, grad_dtype};
-    return bwd_impl(q, k, v, nullptr, dO, lse, delta, nullptr, nullptr, dk, dv, B, T, Hq, Hkv, d, st, scale,
+    return bwd_impl(q, k, v, nullptr, dO, lse, delta, nullptr, dO_absmax, nullptr, nullptr, dk, dv, B, T, Hq, Hkv, d, st, scale,
                     stream, false);
 }
 

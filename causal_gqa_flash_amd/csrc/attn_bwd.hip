@@ -12,11 +12,21 @@
 //   dS = P * (dP - D), dQ = scale * dS K, dK = scale * dS^T Q, dV = P^T dO.
 // In log2 units P = 2^(S * scale * log2(e) - LSE * log2(e)).
 //
-// Precision. All products run on the fp16 matrix core with fp32 accumulation: Q, K,
-// V and dO are converted from bf16 to fp16 (exact for magnitudes in [2^-14, 65504];
-// smaller ones round to fp16 subnormals), and P and dS are rounded to fp16, which
-// carries three more bits than bf16. D has to be accurate to the fp32 level: the one
-// the bf16 output O gives (D~ = dO . O_bf16) is off by the rounding of O, and that error
+// Precision. The products that take P or dS run on the fp16 matrix core with fp32
+// accumulation: their other operands are converted from bf16 to fp16 (exact for
+// magnitudes in [2^-14, 65504]), and P and dS are rounded to fp16, which carries three
+// more bits than bf16. dS and dO scale with the loss: gradients into attention are often
+// far below fp16's normal range (2^-14). So they are scaled by exact powers of two before
+// the rounding and the products are scaled back in fp32 at the end: in the dQ kernel each
+// query row by the inverse of its own largest |dO| (dQ row i only sums row i's terms); in
+// the dK/dV kernel, whose sums run over many query rows, every row of a (batch, kv head)
+// group by one scale, the one that brings the group's largest |dO| into [1, 2). The dQ
+// kernel, which reads every dO row anyway, publishes the largest |dO| of each block of
+// 32 rows; the dK/dV kernel reduces its group's blocks before its loop. Scaled dO then
+// stays below 2 and dS below 65504 as long as every row of V has sum_c |V_c| < 16000.
+// Power-of-two scaling commutes with rounding in the normal range, so a power-of-two
+// factor on dO moves every gradient by exactly that factor.
+// D has to be accurate to the fp32 level: the one the bf16 output O gives (D~ = dO . O_bf16) is off by the rounding of O, and that error
 // is multiplied by K in dQ and by Q in dK. The dQ kernel therefore forms dS~ with D~
 // (known before its loop), accumulates the exact D = sum_j P_ij dP_ij on the side and
 // K_bar = sum_j P_ij K_j with one more product, and finishes with
@@ -105,11 +115,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     // exactly as in fp16; the products with computed P and dS~ use K in fp16.
     f16x8 qreg[NQB][C::kKD];
     bf16x8 doreg[NQB][C::kKD];
-    float dtilde[NQB], lse2[NQB], dexact[NQB];
+    float dtilde[NQB], lse2[NQB], dexact[NQB], dsc[NQB], dsc_inv[NQB], dts[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
         const int row = qw + 32 * qb + n;
         float part = 0.0f;
+        unsigned dmax = 0;
 #pragma unroll
         for (int kd = 0; kd < C::kKD; ++kd) {
             u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u}, xo = {0u, 0u, 0u, 0u};
@@ -121,6 +132,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
             }
             qreg[qb][kd] = bf16x8_to_f16(xq);
             doreg[qb][kd] = __builtin_bit_cast(bf16x8, xd);
+            dmax = max(dmax, bf16x8_absmax_bits(xd));
             const bf16x8 dv8 = __builtin_bit_cast(bf16x8, xd);
             const bf16x8 ov8 = __builtin_bit_cast(bf16x8, xo);
 #pragma unroll
@@ -128,6 +140,17 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
         }
         part += swap_halves(part);
         dtilde[qb] = part;
+        // dS of this row is scaled by 2^k (largest |dO| of the row into [1, 2)) before its
+        // fp16 rounding, and dQ~ scaled back at the store.
+        dmax = max(dmax, (unsigned)__shfl_xor((int)dmax, 32, 64));
+        // The block's largest |dO| (its 32 rows), published for the dK/dV pass.
+        const unsigned bmax = wave_max_u32(dmax);
+        if (lane == 0 && qw + 32 * qb < T)
+            a.do_absmax[((size_t)b * Hq + h) * ((T + 31) / 32) + (qw + 32 * qb) / 32] = __uint_as_float(bmax << 16);
+        const Pow2Scale ps = pow2_normalizer(dmax);
+        dsc[qb] = ps.s;
+        dsc_inv[qb] = ps.inv;
+        dts[qb] = part * ps.s;
         dexact[qb] = 0.0f;
         lse2[qb] = row < T ? a.lse[((size_t)b * Hq + h) * T + row] * kLog2e : 0.0f;
     }
@@ -213,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
                         if (rel + 32 * kb + 8 * (i >> 2) + (i & 3) > 0) p = 0.0f;
                     }
                     dexact[qb] = fmaf(p, dp[kb][qb][i], dexact[qb]);
-                    dp[kb][qb][i] = p * (dp[kb][qb][i] - dtilde[qb]);
+                    dp[kb][qb][i] = p * fmaf(dp[kb][qb][i], dsc[qb], -dts[qb]);
                     s[kb][qb][i] = p;
                 }
             }
@@ -286,7 +309,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
                 f32x4 x;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    x[r] = a.scale * fmaf(-corr, kbar[qb][mb][4 * u + r], dqacc[qb][mb][4 * u + r]);
+                    x[r] = a.scale * fmaf(-corr, kbar[qb][mb][4 * u + r], dqacc[qb][mb][4 * u + r] * dsc_inv[qb]);
                 if (a.rope_cos) x = rope_back4(x, rt[mb][u]);
                 store_out4(a.dq, drow + 32 * mb + 8 * u + 4 * hl, x, a.grad_bf16);
             }
@@ -350,6 +373,8 @@ template <int D, int BQ, int NKW, int HS, int NR, bool SAME_QDO, bool BF16OUT, b
 __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) {
     using C = DkvCfg<D, BQ, NKW, HS, NR>;
     __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
+    __shared__ unsigned wg_red[C::kThreads / 64];   // one word per wave: the dO scale search
+    __shared__ float sigma_sh;                      // the dO scale (see below)
 
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
     const int G = Hq / Hkv;
@@ -471,8 +496,15 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
         }
         advance(dma_cur);
     };
+    // dO (and with it dP, delta and dS) is multiplied by the workgroup's power-of-two scale
+    // sigma before its fp16 rounding; dK and dV are multiplied back by 1 / sigma at the
+    // store (see the header). The loop reads sigma from LDS at each conversion instead of
+    // keeping it in a register: the loop sits at the register budget of three waves per
+    // SIMD, and one more live value there makes the compiler trade the products'
+    // overlap with the softmax for register pressure (measured: about 7% slower).
+    auto load_sigma = [&]() CGQA_INLINE { return sigma_sh; };
     // Raw step -> converted step (fp16 rows, scaled and masked statistics).
-    auto convert_step = [&](int st) CGQA_INLINE {
+    auto convert_step = [&](int st, float sigma) CGQA_INLINE {
         const char* raw = slot_base + cvt_cur.stage * C::kRawStage;
         char* cv = conv_stage(st);
         const int qs0 = cvt_cur.q0;
@@ -484,7 +516,8 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
                 const int ch = stid + i * C::kSlotThreads;
                 const int row = ch / (C::kRawRow / 16), col = ch % (C::kRawRow / 16);
                 const u32x4 x = *reinterpret_cast<const u32x4*>(raw + t * C::kRawTile + ch * 16);
-                store16(cv + t * C::kTile + row * C::kPitch + col * 16, bf16x8_to_f16_bits(x));
+                store16(cv + t * C::kTile + row * C::kPitch + col * 16,
+                        t == 0 ? bf16x8_to_f16_bits(x) : bf16x8_to_f16_bits_scaled(x, sigma));
             }
         }
         if (stid < 2 * BQ) {
@@ -492,7 +525,7 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
             const bool valid = qs0 + (stid % BQ) < T;
             float y;
             if (stid < BQ) y = valid ? x * kLog2e : INFINITY;    // P = 0 past T
-            else y = valid ? x : 0.0f;
+            else y = valid ? x * sigma : 0.0f;
             reinterpret_cast<float*>(cv + 2 * C::kTile)[stid] = y;
         }
     };
@@ -504,9 +537,21 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     };
 
     // Prologue: DMA step 0, then load K and V of the lane's key as B operands (dims
-    // 16*kd + 8*hl .. +7) in fp16, so the two latencies overlap; only these are waited
-    // for before the later steps are issued.
+    // 16*kd + 8*hl .. +7) in fp16, and the dO block maxima of the group, so the
+    // latencies overlap; only these are waited for before the later steps are issued.
     if (nsteps > 0) issue_step();
+    // The scale: the largest |dO| over every query row of the group's heads (published
+    // by attn_bwd_dq per block of 32 rows; non-negative floats, so their bit patterns
+    // order like the values), into [1, 2). Every workgroup of a (batch, kv head) group
+    // gets the same scale, whatever the grid.
+    {
+        const int nblk = (T + 31) / 32;
+        const float* am = a.do_absmax + ((size_t)b * Hq + (size_t)g * G) * nblk;
+        unsigned bits = 0;
+        for (int i = tid; i < G * nblk; i += C::kThreads) bits = max(bits, __float_as_uint(am[i]) >> 16);
+        const unsigned wmax = wave_max_u32(bits);
+        if (lane == 0) wg_red[wave] = wmax;
+    }
     f16x8 kreg[C::kKD], vreg[C::kKD];
 #pragma unroll
     for (int kd = 0; kd < C::kKD; ++kd) {
@@ -530,8 +575,15 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     for (int mb = 0; mb < C::kMB; ++mb) { dkacc[mb] = zero16(); dvacc[mb] = zero16(); }
 
     wait_tiles_barrier<0>();
-    for (int st = 1; st < NR && st < nsteps; ++st) issue_step();
-    if (nsteps > 0) convert_step(0);
+    {
+        unsigned m = 0;
+#pragma unroll
+        for (int w = 0; w < C::kThreads / 64; ++w) m = max(m, wg_red[w]);
+        const float sigma = pow2_normalizer(__builtin_amdgcn_readfirstlane(m)).s;
+        if (tid == 0) sigma_sh = sigma;      // read in the loop, after its first barrier
+        for (int st = 1; st < NR && st < nsteps; ++st) issue_step();
+        if (nsteps > 0) convert_step(0, sigma);
+    }
 
     const int tr_row = (lane & 15) >> 2;
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -594,7 +646,7 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
         if (step + NR < nsteps) issue_step();
     };
     auto convert_next = [&](int step) CGQA_INLINE {
-        if (step + 1 < nsteps) convert_step(step + 1);
+        if (step + 1 < nsteps) convert_step(step + 1, load_sigma());
     };
     auto compute_step = [&](auto Mc, int step) CGQA_INLINE {
         const char* qs = conv_stage(step);
@@ -688,8 +740,9 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
             }
         }
     };
-    reduce_store(dkacc, a.dk, a.scale, std::integral_constant<bool, ROPE>{});
-    reduce_store(dvacc, a.dv, 1.0f, std::false_type{});
+    const float sigma_inv = 1.0f / load_sigma();   // exact: a power of two
+    reduce_store(dkacc, a.dk, a.scale * sigma_inv, std::integral_constant<bool, ROPE>{});
+    reduce_store(dvacc, a.dv, sigma_inv, std::false_type{});
 }
 
 // ---- Software-pipelined dQ (d = 64) ---------------------------------------------------
@@ -780,10 +833,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
     // Q, dO (bf16, as given) as B operands (lane: query n, dims 16*kd + 8*hl .. +7),
     // D~ = rowsum(dO * O) from the given bf16 O, and the row's LSE in log2 units.
     bf16x8 qreg[C::kKD], doreg[C::kKD];
-    float dtilde, lse2, dexact = 0.0f;
+    float dtilde, lse2, dexact = 0.0f, dsc, dsc_inv, dts;
     {
         const int row = qw + n;
         float part = 0.0f;
+        unsigned dmax = 0;
 #pragma unroll
         for (int kd = 0; kd < C::kKD; ++kd) {
             u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u}, xo = {0u, 0u, 0u, 0u};
@@ -796,6 +850,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
             }
             qreg[kd] = __builtin_bit_cast(bf16x8, xq);
             doreg[kd] = __builtin_bit_cast(bf16x8, xd);
+            dmax = max(dmax, bf16x8_absmax_bits(xd));
             const bf16x8 dv8 = __builtin_bit_cast(bf16x8, xd);
             const bf16x8 ov8 = __builtin_bit_cast(bf16x8, xo);
 #pragma unroll
@@ -803,6 +858,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
         }
         part += swap_halves(part);
         dtilde = part;
+        // dS of this row is scaled by 2^k (largest |dO| of the row into [1, 2)) before its
+        // fp16 rounding, and dQ~ scaled back at the store.
+        dmax = max(dmax, (unsigned)__shfl_xor((int)dmax, 32, 64));
+        // The block's largest |dO| (its 32 rows), published for the dK/dV pass.
+        const unsigned bmax = wave_max_u32(dmax);
+        if (lane == 0 && qw < T) a.do_absmax[((size_t)b * Hq + h) * ((T + 31) / 32) + qw / 32] = __uint_as_float(bmax << 16);
+        const Pow2Scale ps = pow2_normalizer(dmax);
+        dsc = ps.s;
+        dsc_inv = ps.inv;
+        dts = part * ps.s;
         lse2 = row < T ? a.lse[((size_t)b * Hq + h) * T + row] * kLog2e : 0.0f;
 #pragma unroll
         for (int kd = 0; kd < C::kKD; ++kd) asm volatile("" ::"v"(qreg[kd]), "v"(doreg[kd]));
@@ -874,7 +939,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
             if constexpr (MAY_MASK)
                 if (diag && rel + 8 * (i >> 2) + (i & 3) > 0) e = 0.0f;
             dexact = fmaf(e, dpc[i], dexact);
-            dpc[i] = e * (dpc[i] - dtilde);
+            dpc[i] = e * fmaf(dpc[i], dsc, -dts);
             sc[i] = e;
         }
         pk[0] = pack_lo_f16(sc);
@@ -949,7 +1014,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
             for (int u = 0; u < 4; ++u) {
                 f32x4 x;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) x[r] = a.scale * fmaf(-corr, kbar[mb][4 * u + r], dqacc[mb][4 * u + r]);
+                for (int r = 0; r < 4; ++r) x[r] = a.scale * fmaf(-corr, kbar[mb][4 * u + r], dqacc[mb][4 * u + r] * dsc_inv);
                 if (a.rope_cos) x = rope_back4(x, rt[mb][u]);
                 store_out4(a.dq, drow + 32 * mb + 8 * u + 4 * hl, x, a.grad_bf16);
             }

@@ -31,6 +31,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __fp16 fp16x4_raw __attribute__((__vector_size__(4 * sizeof(__fp16))));
@@ -95,6 +96,16 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16(const u32x4& w) {
 __device__ __forceinline__ u32x4 bf16x8_to_f16_bits(const u32x4& w) {
     return __builtin_bit_cast(u32x4, bf16x8_to_f16(w));
 }
+// The same values times a power of two `s` (exact in fp32) before the fp16 rounding.
+__device__ __forceinline__ u32x4 bf16x8_to_f16_bits_scaled(const u32x4& w, float s) {
+    f32x8 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __builtin_bit_cast(float, w[i] << 16) * s;
+        f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u) * s;
+    }
+    return __builtin_bit_cast(u32x4, __builtin_convertvector(f, f16x8));
+}
 
 // Eight accumulator registers (base .. base+7) rounded to bf16 (round to nearest
 // even, v_cvt_pk_bf16_f32), in register order.
@@ -110,6 +121,41 @@ __device__ __forceinline__ f16x8 pack_lo_f16(const f32x16& c) {
 }
 __device__ __forceinline__ f16x8 pack_hi_f16(const f32x16& c) {
     return __builtin_convertvector(c.hi, f16x8);
+}
+
+// The largest magnitude among eight bf16 values (as loaded, two per 32-bit word), as its
+// bit pattern without the sign: for finite values the bit patterns order like the
+// magnitudes.
+__device__ __forceinline__ unsigned bf16x8_absmax_bits(const u32x4& w) {
+    u16x2 m = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+    return max((unsigned)m[0], (unsigned)m[1]);
+}
+
+// Largest value over the wave, on every lane: DPP swaps within quads, then the two
+// mirrors fold each row of 16 lanes; the four row maxima are read as scalars.
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
+    v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    const unsigned r0 = (unsigned)__builtin_amdgcn_readlane((int)v, 0), r1 = (unsigned)__builtin_amdgcn_readlane((int)v, 16);
+    const unsigned r2 = (unsigned)__builtin_amdgcn_readlane((int)v, 32), r3 = (unsigned)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// An exact power-of-two scale that brings a value whose largest bf16 magnitude has the bit
+// pattern `bits` into [1, 2), and its inverse: 2^(127 - E) and 2^(E - 127) for the value's
+// exponent field E, clamped to [1, 253] so that both are normal fp32 numbers (a zero or
+// subnormal maximum takes the largest scale). Multiplying by either is exact, and fp16
+// rounding commutes with it wherever the values stay in fp16's normal range.
+struct Pow2Scale {
+    float s, inv;
+};
+__device__ __forceinline__ Pow2Scale pow2_normalizer(unsigned bits) {
+    const int e = min(max((int)(bits >> 7), 1), 253);
+    return {__uint_as_float((unsigned)(254 - e) << 23), __uint_as_float((unsigned)e << 23)};
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -32,6 +32,7 @@ struct BwdArgs {
     const uint16_t* dO;
     const float* lse;
     float* delta;       // written by the dq kernel, read by the dkv kernel
+    float* do_absmax;   // [B][Hq][ceil(T/32)]: largest |dO| per 32-row block (dq writes, dkv reads)
     void* dq;           // fp32, or bf16 when grad_bf16
     void* dk;
     void* dv;

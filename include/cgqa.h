@@ -18,6 +18,8 @@
  *                              scale * q.k over keys 0..i (causal, inclusive)
  *   delta    : [B][Hq][T]      float32, D_i = sum_j P_ij dP_ij (= sum_c dO[i,c] * O[i,c]
  *                              in exact arithmetic)
+ *   dO_absmax: [B][Hq][NB]     float32, NB = ceil(T / 32): the largest |dO| over the 32
+ *                              query rows 32*j .. 32*j+31 of head h (rows below T)
  *   dq       : [B][T][Hq][d]   float32
  *   dk, dv   : [B][T][Hkv][d]  float32
  * Query head h uses key/value head h / (Hq / Hkv). Query i sees keys 0..i.
@@ -30,6 +32,19 @@
  * value. Calls allocate nothing, keep no state between calls and may be made from
  * several host threads at once. Outputs must not overlap inputs or each other.
  * B == 0 or T == 0 is an empty problem: the call succeeds and touches nothing.
+ *
+ * Numerics and value range. The forward's two products run on the bf16 matrix cores
+ * with fp32 accumulation and an fp32 softmax. The backward's products that take the
+ * probabilities P or dS = P (dP - D) run on the fp16 matrix cores with fp32
+ * accumulation, so q, k and v are converted to fp16 there: their magnitudes must stay
+ * below 65504 (beyond it gradients turn infinite), and values under 2^-14 keep fewer
+ * significant bits than bf16 gives them. dO may have any bf16 magnitude, also one that
+ * differs widely from row to row: before their fp16 rounding, dO and dS are scaled by
+ * powers of two (per query row in attn_bwd_dq; in attn_bwd_dkv by one scale per batch and
+ * key/value head, from the largest |dO| of the group's query heads, which attn_bwd_dq
+ * publishes in dO_absmax) and the sums are scaled back in fp32. Multiplying dO by 2^k
+ * therefore multiplies delta, dq, dk and dv by exactly 2^k, short of fp32 underflow or
+ * overflow. dS stays finite whenever every row of v has sum_c |v_c| < 16000.
  *
  * Return value: CGQA_OK (0) or one of the codes below. All argument checks happen
  * before any HIP call, so a rejected call has touched neither the device nor the
@@ -71,22 +86,24 @@ int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 /* Backward, query side (section "The same bits every time": each block of queries
  * has a single owning workgroup). For the loss L = sum(O * dO): recomputes P from q, k
  * and lse, writes delta = D_i = sum_j P_ij dP_ij (accumulated in fp32 inside the kernel;
- * it equals rowsum(dO * O), which the bf16 o would give only to bf16 accuracy) and
- * dq = dL/dq. Reads q, k, v, o, dO, lse; overwrites delta and dq. */
+ * it equals rowsum(dO * O), which the bf16 o would give only to bf16 accuracy),
+ * dO_absmax (the caller-owned workspace that carries the scale of dO to attn_bwd_dkv,
+ * B*Hq*ceil(T/32) floats) and dq = dL/dq. Reads q, k, v, o, dO, lse; overwrites delta,
+ * dO_absmax and dq. */
 int attn_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 const uint16_t* o, const uint16_t* dO, const float* lse,
-                float* delta, float* dq,
+                float* delta, float* dO_absmax, float* dq,
                 int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
 
 /* Backward, key side (same section: each block of keys has a single owning workgroup,
  * which visits the query heads of its key/value head's group in ascending order and,
  * for each, the query blocks in ascending order). Writes dk = dL/dk and dv = dL/dv, summed over the
- * group. Reads the delta written by attn_bwd_dq, so it must be enqueued after that
- * call on the same stream (or after an event recorded behind it).
- * Reads q, k, v, dO, lse, delta; overwrites dk and dv. */
+ * group. Reads the delta and dO_absmax written by attn_bwd_dq for the same dO, so it
+ * must be enqueued after that call on the same stream (or after an event recorded
+ * behind it). Reads q, k, v, dO, lse, delta, dO_absmax; overwrites dk and dv. */
 int attn_bwd_dkv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                  const uint16_t* dO, const float* lse, const float* delta,
-                 float* dk, float* dv,
+                 const float* dO_absmax, float* dk, float* dv,
                  int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
 
 /* Strided variants: the same operations on tensors that sit inside wider rows, e.g. the
@@ -105,7 +122,7 @@ int attn_bwd_dkv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *
  * grad_dtype selects the type of dq, dk and dv: CGQA_GRAD_F32 (float) or CGQA_GRAD_BF16
  * (bfloat16 bit patterns, rounded to nearest even from the same float values the float
- * outputs hold). lse and delta stay [B][Hq][T] float32.
+ * outputs hold). lse and delta stay [B][Hq][T] float32, dO_absmax [B][Hq][ceil(T/32)].
  *
  * Outputs may share a buffer with each other when their row strides (in bytes) are
  * equal and their column ranges within a row do not meet (dq, dk, dv of one packed
@@ -120,7 +137,7 @@ int attn_fwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 int attn_bwd_dq_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const uint16_t* o, const uint16_t* dO, const float* lse,
-                        float* delta, void* dq,
+                        float* delta, float* dO_absmax, void* dq,
                         int B, int T, int Hq, int Hkv, int d,
                         int q_row_stride, int kv_row_stride, int o_row_stride,
                         int do_row_stride, int dq_row_stride, int grad_dtype,
@@ -128,7 +145,7 @@ int attn_bwd_dq_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 int attn_bwd_dkv_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const uint16_t* dO, const float* lse, const float* delta,
-                         void* dk, void* dv,
+                         const float* dO_absmax, void* dk, void* dv,
                          int B, int T, int Hq, int Hkv, int d,
                          int q_row_stride, int kv_row_stride, int do_row_stride,
                          int dkv_row_stride, int grad_dtype, float scale, void* stream);
@@ -150,7 +167,7 @@ int attn_bwd_dkv_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v
  * (contiguous, fp32 gradients) whose dq and dk are turned back inside the kernels, before
  * they are stored, to the gradients with respect to the unrotated q and k:
  *   g[2i] = gy[2i] cos + gy[2i+1] sin,   g[2i+1] = -gy[2i] sin + gy[2i+1] cos
- * (dv and delta are unchanged). */
+ * (dv, delta and dO_absmax are unchanged). */
 int attn_rope_qk(const uint16_t* q, const uint16_t* k, uint16_t* q_out, uint16_t* k_out,
                  const float* cos, const float* sin, int B, int T, int Hq, int Hkv, int d,
                  int q_row_stride, int k_row_stride, int q_out_row_stride, int k_out_row_stride,
@@ -158,12 +175,12 @@ int attn_rope_qk(const uint16_t* q, const uint16_t* k, uint16_t* q_out, uint16_t
 
 int attn_bwd_dq_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      const uint16_t* o, const uint16_t* dO, const float* lse,
-                     float* delta, float* dq, const float* cos, const float* sin,
+                     float* delta, float* dO_absmax, float* dq, const float* cos, const float* sin,
                      int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
 
 int attn_bwd_dkv_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const uint16_t* dO, const float* lse, const float* delta,
-                      float* dk, float* dv, const float* cos, const float* sin,
+                      const float* dO_absmax, float* dk, float* dv, const float* cos, const float* sin,
                       int B, int T, int Hq, int Hkv, int d, float scale, void* stream);
 
 /* Naive attention, the GPU reference mode (page "A transformer in PTX", section "Three

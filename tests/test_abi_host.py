@@ -52,15 +52,17 @@ def call_fwd(ptrs=None, **kw):
     return cg.library().attn_fwd(*p, a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["scale"], None)
 
 
+# The backward calls take 9 pointers: dq: q k v o dO lse | delta dO_absmax dq;
+# dkv: q k v dO lse delta dO_absmax | dk dv.
 def call_dq(ptrs=None, **kw):
     a = dict(GOOD, **kw)
-    p = ptrs or [fake(i) for i in range(8)]
+    p = ptrs or [fake(i) for i in range(9)]
     return cg.library().attn_bwd_dq(*p, a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["scale"], None)
 
 
 def call_dkv(ptrs=None, **kw):
     a = dict(GOOD, **kw)
-    p = ptrs or [fake(i) for i in range(8)]
+    p = ptrs or [fake(i) for i in range(9)]
     return cg.library().attn_bwd_dkv(*p, a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["scale"], None)
 
 
@@ -87,7 +89,7 @@ def test_bad_shapes_rejected(call, kw, code):
     assert call(**kw) == code
 
 
-@pytest.mark.parametrize("call,n", [(call_fwd, 5), (call_dq, 8), (call_dkv, 8)])
+@pytest.mark.parametrize("call,n", [(call_fwd, 5), (call_dq, 9), (call_dkv, 9)])
 def test_null_pointers_rejected(call, n):
     for i in range(n):
         p = [fake(j) for j in range(n)]
@@ -95,7 +97,7 @@ def test_null_pointers_rejected(call, n):
         assert call(ptrs=p) == cg.CGQA_EINVAL, i
 
 
-@pytest.mark.parametrize("call,n", [(call_fwd, 5), (call_dq, 8), (call_dkv, 8)])
+@pytest.mark.parametrize("call,n", [(call_fwd, 5), (call_dq, 9), (call_dkv, 9)])
 def test_misaligned_pointers_rejected(call, n):
     for i in range(n):
         p = [fake(j) for j in range(n)]
@@ -103,15 +105,15 @@ def test_misaligned_pointers_rejected(call, n):
         assert call(ptrs=p) == cg.CGQA_EUNSUPPORTED, i
 
 
-@pytest.mark.parametrize("call,n,outs", [(call_fwd, 5, (3, 4)), (call_dq, 8, (6, 7)),
-                                         (call_dkv, 8, (6, 7))])
+@pytest.mark.parametrize("call,n,outs", [(call_fwd, 5, (3, 4)), (call_dq, 9, (6, 7, 8)),
+                                         (call_dkv, 9, (7, 8))])
 def test_overlapping_outputs_rejected(call, n, outs):
     for o in outs:
         for other in range(n):
             if other == o:
                 continue
             p = [fake(j) for j in range(n)]
-            p[o] = p[other] + 64          # inside the other buffer
+            p[o] = p[other] + 16          # inside the other buffer (the smallest, dO_absmax, is 48 bytes)
             assert call(ptrs=p) == cg.CGQA_EINVAL, (o, other)
 
 
@@ -120,7 +122,7 @@ def test_empty_problem_is_a_no_op(call):
     # Empty problems succeed without a HIP call, also with null pointers.
     assert call(B=0) == cg.CGQA_OK
     assert call(T=0) == cg.CGQA_OK
-    assert call(ptrs=[None] * (5 if call is call_fwd else 8), T=0) == cg.CGQA_OK
+    assert call(ptrs=[None] * (5 if call is call_fwd else 9), T=0) == cg.CGQA_OK
     assert call(B=0, d=32) == cg.CGQA_EUNSUPPORTED   # shape errors still win
 
 
@@ -152,7 +154,7 @@ def call_fwd_s(ptrs=None, st=None, **kw):
 def call_dq_s(ptrs=None, st=None, **kw):
     a = dict(GOOD, **kw)
     s = strides(a, **(st or {}))
-    p = ptrs or [fake(i) for i in range(8)]
+    p = ptrs or [fake(i) for i in range(9)]
     return cg.library().attn_bwd_dq_strided(*p, a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], s["q_rs"],
                                             s["kv_rs"], s["o_rs"], s["do_rs"], s["dq_rs"], s["grad"],
                                             a["scale"], None)
@@ -161,12 +163,12 @@ def call_dq_s(ptrs=None, st=None, **kw):
 def call_dkv_s(ptrs=None, st=None, **kw):
     a = dict(GOOD, **kw)
     s = strides(a, **(st or {}))
-    p = ptrs or [fake(i) for i in range(8)]
+    p = ptrs or [fake(i) for i in range(9)]
     return cg.library().attn_bwd_dkv_strided(*p, a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], s["q_rs"],
                                              s["kv_rs"], s["do_rs"], s["dkv_rs"], s["grad"], a["scale"], None)
 
 
-STRIDED = [(call_fwd_s, 5, (3, 4)), (call_dq_s, 8, (6, 7)), (call_dkv_s, 8, (6, 7))]
+STRIDED = [(call_fwd_s, 5, (3, 4)), (call_dq_s, 9, (6, 7, 8)), (call_dkv_s, 9, (7, 8))]
 
 
 @pytest.mark.parametrize("call", [c for c, _, _ in STRIDED])
@@ -188,7 +190,7 @@ def test_strided_null_misaligned_overlapping_rejected(call, n, outs):
         for other in range(n):
             if other != o:
                 p = [fake(j) for j in range(n)]
-                p[o] = p[other] + 64
+                p[o] = p[other] + 16
                 assert call(ptrs=p) == cg.CGQA_EINVAL, (o, other)
 
 
@@ -221,15 +223,15 @@ def test_packed_gradients_must_not_share_columns():
     # dk and dv in one buffer with row stride R = (Hq + 2 Hkv) d = 640 floats: dv placed
     # 64 bytes after dk lies inside dk's 128 columns of every row.
     R = 640
-    p = [fake(j) for j in range(8)]
-    p[7] = p[6] + 64
+    p = [fake(j) for j in range(9)]
+    p[8] = p[7] + 64
     assert call_dkv_s(ptrs=p, st={"dkv_rs": R}) == cg.CGQA_EINVAL
     # bf16 dv one row-window too far: its columns [96, 224) meet dk's [0, 128)
-    p[7] = p[6] + 2 * 96
+    p[8] = p[7] + 2 * 96
     assert call_dkv_s(ptrs=p, st={"dkv_rs": R, "grad": 1}) == cg.CGQA_EINVAL
     # dq written into the input q buffer's rows (q's columns) is an overlap
-    p = [fake(j) for j in range(8)]
-    p[7] = p[0] + 16
+    p = [fake(j) for j in range(9)]
+    p[8] = p[0] + 16
     assert call_dq_s(ptrs=p, st={"q_rs": 640, "dq_rs": 320}) == cg.CGQA_EINVAL
 
 
@@ -413,15 +415,15 @@ def test_rope_rejections():
 def test_rope_backward_rejections():
     lib = cg.library()
     args = (1, 64, 6, 2, 64, 0.125, None)
-    p = [fake(j) for j in range(10)]
+    p = [fake(j) for j in range(11)]
     for fn in (lib.attn_bwd_dq_rope, lib.attn_bwd_dkv_rope):
-        for i in (8, 9):                       # missing table
+        for i in (9, 10):                      # missing table
             q = list(p)
             q[i] = None
             assert fn(*q, *args) == cg.CGQA_EINVAL, i
         q = list(p)
-        q[8] += 8                               # misaligned table
+        q[9] += 8                               # misaligned table
         assert fn(*q, *args) == cg.CGQA_EUNSUPPORTED
         q = list(p)
-        q[8] = q[7] + 64                        # table inside an output
+        q[9] = q[8] + 64                        # table inside an output
         assert fn(*q, *args) == cg.CGQA_EINVAL

@@ -24,7 +24,7 @@ def test_attention_step_replays_bit_exactly():
     bf, f32 = dict(dtype=torch.bfloat16, device="cuda"), dict(dtype=torch.float32, device="cuda")
     qr, kr = torch.empty((B, T, Hq, d), **bf), torch.empty((B, T, Hkv, d), **bf)
     o, lse = torch.empty((B, T, Hq, d), **bf), torch.empty((B, Hq, T), **f32)
-    delta, dq = torch.empty((B, Hq, T), **f32), torch.empty((B, T, Hq, d), **f32)
+    delta, dq = cg.bwd_delta(B, Hq, T, device="cuda"), torch.empty((B, T, Hq, d), **f32)
     dk, dv = torch.empty((B, T, Hkv, d), **f32), torch.empty((B, T, Hkv, d), **f32)
     wq = torch.from_numpy(si.f32_to_bf16_bits(np.random.default_rng(62).standard_normal((640, 384), dtype=np.float32)).view(np.int16)).view(torch.bfloat16).cuda()
     xin = torch.from_numpy(si.f32_to_bf16_bits(np.random.default_rng(63).standard_normal((B * T, 384), dtype=np.float32)).view(np.int16)).view(torch.bfloat16).cuda()
