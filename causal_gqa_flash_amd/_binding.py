@@ -68,6 +68,8 @@ def library():
         lib.attn_bwd_dq_rope.restype = i
         lib.attn_bwd_dkv_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.attn_bwd_dkv_rope.restype = i
+        lib.cgqa_gemm_static.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+        lib.cgqa_gemm_static.restype = i
         lib.cgqa_gemm_workspace_bytes.argtypes = [i, i, i]
         lib.cgqa_gemm_workspace_bytes.restype = ctypes.c_size_t
         lib.cgqa_gemm.restype = i

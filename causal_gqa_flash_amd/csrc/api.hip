@@ -232,8 +232,10 @@ int naive_impl(bool fwd, const uint16_t* q, const uint16_t* k, const uint16_t* v
     return finish(fwd ? cgqa::launch_naive_fwd(a, (hipStream_t)stream) : cgqa::launch_naive_bwd(a, (hipStream_t)stream));
 }
 
+// use_scratch: the split-K partials go to the library's static per-device scratch
+// (cgqa_gemm_static) instead of `ws`; shapes whose split needs more are rejected.
 int gemm_impl(const uint16_t* A, const uint16_t* B, void* C, const float* R, int M, int N, int K, int flags,
-              float* ws, size_t ws_bytes, void* stream) {
+              float* ws, size_t ws_bytes, void* stream, bool use_scratch = false) {
     if (M < 0 || N < 0 || K < 0) return CGQA_EINVAL;
     if (flags & ~(CGQA_GEMM_A_KM | CGQA_GEMM_B_KN | CGQA_GEMM_C_BF16)) return CGQA_EINVAL;
     const bool akm = flags & CGQA_GEMM_A_KM, bkn = flags & CGQA_GEMM_B_KN, cbf = flags & CGQA_GEMM_C_BF16;
@@ -249,6 +251,12 @@ int gemm_impl(const uint16_t* A, const uint16_t* B, void* C, const float* R, int
     const View va{A, 1, (int64_t)M * K, (int64_t)M * K, 2}, vb{B, 1, (int64_t)N * K, (int64_t)N * K, 2};
     if (!disjoint(vc, va) || !disjoint(vc, vb)) return CGQA_EINVAL;
     if (R && (const void*)R != C && !disjoint(vc, View{R, 1, (int64_t)M * N, (int64_t)M * N, 4})) return CGQA_EINVAL;
+    size_t need = 0;
+    if (use_scratch) {
+        need = (size_t)cgqa::gemm_splits(M, N, K, (size_t)-1);
+        need = need > 1 ? need * cgqa::gemm_slice_floats(M, N) * 4 : 0;
+        if (need > cgqa::kGemmScratchBytes) return CGQA_EINVAL;
+    }
     if (ws) {
         if (!aligned16(ws)) return CGQA_EUNSUPPORTED;
         const int64_t n = (int64_t)(ws_bytes / 4);
@@ -262,6 +270,13 @@ int gemm_impl(const uint16_t* A, const uint16_t* B, void* C, const float* R, int
     a.M = M; a.N = N; a.K = K;
     a.a_km = akm; a.b_kn = bkn; a.c_bf16 = cbf;
     a.ws = ws; a.ws_bytes = ws ? ws_bytes : 0;
+    if (use_scratch && need > 0) {
+        float* p = nullptr;
+        const hipError_t e = cgqa::gemm_scratch(&p);
+        if (e != hipSuccess) return finish(e);
+        a.ws = p;
+        a.ws_bytes = need;
+    }
     return finish(cgqa::launch_gemm(a, (hipStream_t)stream));
 }
 
@@ -338,6 +353,13 @@ size_t cgqa_gemm_workspace_bytes(int M, int N, int K) {
 int cgqa_gemm(const uint16_t* A, const uint16_t* B, void* C, const float* R, int M, int N, int K, int flags,
               float* workspace, size_t workspace_bytes, void* stream) {
     return gemm_impl(A, B, C, R, M, N, K, flags, workspace, workspace_bytes, stream);
+}
+
+static_assert(cgqa::kGemmScratchBytes == CGQA_GEMM_STATIC_SCRATCH_BYTES, "scratch size");
+
+int cgqa_gemm_static(const uint16_t* A, const uint16_t* B, void* C, const float* R, int M, int N, int K,
+                     int flags, void* stream) {
+    return gemm_impl(A, B, C, R, M, N, K, flags, nullptr, 0, stream, true);
 }
 
 size_t attn_naive_workspace_bytes(int B, int T, int Hq) {

@@ -83,6 +83,10 @@ struct GemmArgs {
 };
 // Splits of K the launcher uses for this shape and workspace size (1: none).
 int gemm_splits(int M, int N, int K, size_t ws_bytes);
+// Bytes of the static split-K scratch of the allocation-free GEMM (per device), and its
+// device address on the current device (looked up once per device).
+constexpr size_t kGemmScratchBytes = (size_t)16 << 20;
+hipError_t gemm_scratch(float** ptr);
 // Floats per split's partial product in the workspace: M*N rounded up to a multiple of 4.
 __host__ __device__ inline size_t gemm_slice_floats(int M, int N) { return ((size_t)M * N + 3) & ~(size_t)3; }
 

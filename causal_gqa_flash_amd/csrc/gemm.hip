@@ -26,6 +26,8 @@
 // tile, each writing its fp32 partial product, and a second kernel adds the S partials
 // in split order (and R) into C. The split count is a function of M, N, K and the
 // workspace size only, so results are repeatable.
+#include <mutex>
+
 #include "cgqa_device.hpp"
 #include "cgqa_launch.hpp"
 
@@ -285,6 +287,36 @@ int gemm_splits(int M, int N, int K, size_t ws_bytes) {
     if (s < 2) return 1;
     const int kps = (nk + (int)s - 1) / (int)s;
     return (nk + kps - 1) / kps;   // no empty split
+}
+
+// Scratch of the allocation-free entry point: the split-K partials of cgqa_gemm_static
+// live in this file-scope array, one copy per GPU, which the library holds until the
+// process ends and which every such call on that GPU shares. In host code its name
+// stands for a host-side shadow, not a device address: kernels get the address that
+// hipGetSymbolAddress returns, looked up once per device (with that device current)
+// and kept per device.
+static __device__ __align__(256) float scratch[kGemmScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+float* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t gemm_scratch(float** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? static_cast<float*>(p) : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_gemm(const GemmArgs& a0, hipStream_t stream) {

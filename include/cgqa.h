@@ -244,6 +244,24 @@ int cgqa_gemm(const uint16_t* A, const uint16_t* B, void* C, const float* R,
               int M, int N, int K, int flags, float* workspace, size_t workspace_bytes,
               void* stream);
 
+/* For callers that cannot allocate: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. cgqa_gemm_static is cgqa_gemm without a workspace
+ * argument: a K split keeps its fp32 partials in a device array of
+ * CGQA_GEMM_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on until the
+ * process ends. C comes out bit for bit as from cgqa_gemm given a workspace of at least
+ * cgqa_gemm_workspace_bytes(M, N, K) bytes. A shape whose split needs more than the array
+ * holds (cgqa_gemm_workspace_bytes(M, N, K) > CGQA_GEMM_STATIC_SCRATCH_BYTES) is
+ * CGQA_EINVAL, checked before any HIP call; the other argument rules are cgqa_gemm's. The
+ * call allocates and frees nothing. Every call on one GPU shares that GPU's array, which
+ * keeps the last call's partials (each split writes its whole slice before it is read,
+ * so nothing needs clearing): calls that may overlap on one GPU, e.g. on two streams
+ * with no ordering between them, race and give wrong results; order them. The first
+ * call on a GPU looks the array's address up on that GPU (no allocation). */
+#define CGQA_GEMM_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+
+int cgqa_gemm_static(const uint16_t* A, const uint16_t* B, void* C, const float* R,
+                     int M, int N, int K, int flags, void* stream);
+
 /* Static description of a return code (never NULL): every call reports failure as a code
  * whose meaning can be printed, the library-side form of the pages' practice of naming each
  * failed call and the error behind it (page "Talking to the GPU", section "One macro for

@@ -427,3 +427,15 @@ def test_rope_backward_rejections():
         q = list(p)
         q[9] = q[8] + 64                        # table inside an output
         assert fn(*q, *args) == cg.CGQA_EINVAL
+
+
+def test_gemm_static_rejects_shapes_beyond_its_scratch():
+    """cgqa_gemm_static keeps split-K partials in a fixed device array: a shape whose
+    split needs more is CGQA_EINVAL before any HIP call; the usual rules still apply."""
+    lib = cg.library()
+    p = [fake(j) for j in range(4)]
+    assert lib.cgqa_gemm_workspace_bytes(1024, 1024, 8192) > (16 << 20)
+    assert lib.cgqa_gemm_static(*p, 1024, 1024, 8192, 0, None) == cg.CGQA_EINVAL
+    assert lib.cgqa_gemm_static(*p, 256, 384, 100, 0, None) == cg.CGQA_EUNSUPPORTED   # K % 32
+    assert lib.cgqa_gemm_static(p[0], p[1], None, None, 256, 384, 8192, 0, None) == cg.CGQA_EINVAL
+    assert lib.cgqa_gemm_static(*p, 0, 384, 8192, 0, None) == cg.CGQA_OK             # empty
