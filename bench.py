@@ -124,6 +124,96 @@ def pmc_summarize(fetch_dir, write_dir, out_path):
     print(json.dumps(out), flush=True)
 
 
+def pmc_counters(dirs):
+    """Per-dispatch averages of the SQ/GRBM counters of rocprofv3 --pmc runs of the
+    profiling workload (one folder per pass) for each attention kernel, with ratios that
+    need no clock: executed matrix-core instructions against the credited ones (S, dP,
+    dV, dK and O per 32x32x16 instruction), LDS bank-conflict cycles per LDS-active cycle,
+    and each wave's cycles spent waiting, issuing VALU or issuing LDS."""
+    import csv
+    import glob
+    import synthetic_inputs as si
+    w = si.WORKLOAD_BY_NAME[WORKLOAD]
+    per = {}
+    for d in dirs:
+        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        for r in csv.DictReader(open(path)):
+            for kern, names in KERNEL_NAMES.items():
+                if any(n + "<" in r["Kernel_Name"] for n in names):
+                    c = per.setdefault(kern, {}).setdefault(r["Counter_Name"], {})
+                    c[r["Dispatch_Id"]] = c.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    credited = {"attn_fwd": 4, "attn_bwd_dq": 6, "attn_bwd_dkv": 8}   # flops per pair / d
+    out = {"workload": WORKLOAD, "kernel_source_hash": kernel_source_hash(), "kernels": {}}
+    for kern, cs in per.items():
+        avg = {n: sum(v.values()) / len(v) for n, v in cs.items()}
+        e = {"counters_per_dispatch": {n: round(x, 1) for n, x in sorted(avg.items())}}
+        if "SQ_INSTS_MFMA" in avg:
+            cred = credited[kern] * w.d * w.causal_pairs / (2 * 32 * 32 * 16)
+            e["mfma_insts_executed_per_credited"] = round(avg["SQ_INSTS_MFMA"] / cred, 4)
+        if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
+            e["lds_bank_conflict_per_active_cycle"] = round(avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_LDS_IDX_ACTIVE"], 4)
+        if avg.get("SQ_WAVE_CYCLES"):
+            for n in ("SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                      "SQ_ACTIVE_INST_ANY"):
+                if n in avg:
+                    e[n.lower() + "_per_wave_cycle"] = round(avg[n] / avg["SQ_WAVE_CYCLES"], 4)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and avg.get("SQ_INSTS_MFMA"):
+            e["mfma_busy_cycles_per_inst"] = round(avg["SQ_VALU_MFMA_BUSY_CYCLES"] / avg["SQ_INSTS_MFMA"], 2)
+        out["kernels"][kern] = e
+    print(json.dumps(out, indent=1), flush=True)
+
+
+def trace_summary(trace_dir):
+    """From a rocprofv3 --kernel-trace folder of a bench run, for the bench workload's
+    launches (each kernel's most frequent grid, the one of the step loops): every launch's
+    average duration; every forward, dQ, dK/dV triple that ran back to back (the step
+    loops) with each kernel's duration inside those steps, the gaps between consecutive
+    kernels, and the span from one step's forward to the next (microseconds)."""
+    import csv
+    import glob
+    import statistics as st
+    path = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)[0]
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+
+    def kind(name):
+        for kern, names in KERNEL_NAMES.items():
+            if any(n + "<" in name for n in names):
+                return kern
+        return None
+    grid = lambda r: (r["Grid_Size_X"], r["Grid_Size_Y"], r["Grid_Size_Z"], r["Kernel_Name"])
+    counts = {}
+    for r in rows:
+        if kind(r["Kernel_Name"]):
+            counts[(kind(r["Kernel_Name"]), grid(r))] = counts.get((kind(r["Kernel_Name"]), grid(r)), 0) + 1
+    main_grid = {}
+    for (k, g), c in counts.items():
+        if c > counts.get((k, main_grid.get(k)), 0):
+            main_grid[k] = g
+    rows = [r for r in rows if kind(r["Kernel_Name"]) and grid(r) == main_grid[kind(r["Kernel_Name"])]]
+    seq = [(kind(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+    order = ["attn_fwd", "attn_bwd_dq", "attn_bwd_dkv"]
+    starts = [i for i in range(len(seq) - 2) if [x[0] for x in seq[i:i + 3]] == order]
+    dur = {k: [] for k in order}
+    gap = {"fwd->dq": [], "dq->dkv": [], "dkv->next fwd": []}
+    span = []
+    for i in starts:
+        for j, k in enumerate(order):
+            dur[k].append((seq[i + j][2] - seq[i + j][1]) / 1e3)
+        gap["fwd->dq"].append((seq[i + 1][1] - seq[i][2]) / 1e3)
+        gap["dq->dkv"].append((seq[i + 2][1] - seq[i + 1][2]) / 1e3)
+        if i + 3 < len(seq) and seq[i + 3][0] == "attn_fwd":
+            gap["dkv->next fwd"].append((seq[i + 3][1] - seq[i + 2][2]) / 1e3)
+            span.append((seq[i + 3][1] - seq[i][1]) / 1e3)
+    f = lambda v: {"median": round(st.median(v), 2), "mean": round(st.mean(v), 2), "n": len(v)} if v else None
+    every = {k: [(e - b) / 1e3 for kk, b, e in seq if kk == k] for k in order}
+    out = {"trace": path, "kernels": {k: main_grid[k][3] + " grid " + "x".join(main_grid[k][:3]) for k in order},
+           "all_launches_us": {k: f(v) for k, v in every.items()},
+           "steps": len(starts), "kernel_us": {k: f(v) for k, v in dur.items()},
+           "gap_us": {k: f(v) for k, v in gap.items()}, "step_span_us": f(span),
+           "kernel_sum_median_us": round(sum(st.median(v) for v in dur.values()), 2) if starts else None}
+    print(json.dumps(out, indent=1), flush=True)
+
+
 def gemm_bench(w, graph_timed):
     """The projections around attention for the workload's B*T tokens (model width Hq*d,
     fused QKV width (Hq + 2 Hkv) d): forward QKV and WO (+ residual), and the QKV
@@ -211,13 +301,24 @@ def main():
     ap.add_argument("--no-naive", action="store_true", help="skip timing the naive reference mode")
     ap.add_argument("--no-gemm", action="store_true", help="skip timing the projection matmuls")
     ap.add_argument("--no-rope", action="store_true", help="skip timing the rotary embedding")
+    ap.add_argument("--no-configs", action="store_true", help="skip timing the other workloads")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="run the short workload that rocprofv3 --pmc profiles (see profiles/)")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output folders into the traffic summary")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="summarise the step loops of a rocprofv3 --kernel-trace folder of a bench run")
+    ap.add_argument("--pmc-counters", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 --pmc folders (SQ counters) of the profiling workload")
     args = ap.parse_args()
     if args.pmc_summarize:
         pmc_summarize(args.pmc_summarize[0], args.pmc_summarize[1], TRAFFIC_FILE)
+        return
+    if args.pmc_counters:
+        pmc_counters(args.pmc_counters)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs on a single MI355X and has no "
@@ -245,14 +346,16 @@ def main():
     dv = torch.empty_like(dk)
     stream = torch.cuda.current_stream()
 
+    # The calls launch on the current stream: `stream` in the timed loops, the capture
+    # stream while a HIP graph of them is captured.
     def fwd():
-        cg.attn_fwd(q, k, v, scale=w.scale, o=o, lse=lse, stream=stream)
+        cg.attn_fwd(q, k, v, scale=w.scale, o=o, lse=lse)
 
     def bwd_dq():
-        cg.attn_bwd_dq(q, k, v, o, do, lse, scale=w.scale, delta=delta, dq=dq, stream=stream)
+        cg.attn_bwd_dq(q, k, v, o, do, lse, scale=w.scale, delta=delta, dq=dq)
 
     def bwd_dkv():
-        cg.attn_bwd_dkv(q, k, v, do, lse, delta, scale=w.scale, dk=dk, dv=dv, stream=stream)
+        cg.attn_bwd_dkv(q, k, v, do, lse, delta, scale=w.scale, dk=dk, dv=dv)
 
     def step():
         fwd()
@@ -328,9 +431,13 @@ def main():
 
     # Whole-step timing: exactly `steps` steps between synchronisations.
     ms_step = timed(step, args.steps)
-    # Per-kernel average launch durations (same stream, back-to-back launches).
-    ms_k = {"attn_fwd": timed(fwd, args.steps), "attn_bwd_dq": timed(bwd_dq, args.steps),
-            "attn_bwd_dkv": timed(bwd_dkv, args.steps)}
+    # Each kernel's average launch duration: a captured HIP graph of `steps` back-to-back
+    # launches of it, replayed (no host dispatch in the timed region; a short kernel timed
+    # in a Python loop is bounded by the host's dispatch of each call instead). The
+    # graph-replayed step is timed the same way.
+    ms_k = {"attn_fwd": graph_timed(fwd, args.steps), "attn_bwd_dq": graph_timed(bwd_dq, args.steps),
+            "attn_bwd_dkv": graph_timed(bwd_dkv, args.steps)}
+    ms_step_graph = graph_timed(step, args.steps)
 
     pairs = w.causal_pairs
     fl = {"attn_fwd": 4 * w.d * pairs, "attn_bwd_dq": 6 * w.d * pairs, "attn_bwd_dkv": 8 * w.d * pairs}
@@ -357,10 +464,11 @@ def main():
         "warmup": args.warmup,
         "settle": {"ms": args.settle_ms, "steps": settle_steps},
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_graph": round(ms_step_graph, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 fwd, fp16 bwd",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
                    "pass": "fwd+bwd", "inputs": "bf16 N(0,1), seed 3"},
@@ -368,7 +476,11 @@ def main():
         "fwd_pct_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
         "bwd_tflops": round(bwd_tflops, 2),
         "fwdbwd_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "compute": "fwd bf16 matrix core; bwd fp16 matrix core; fp32 accumulation and softmax",
+        "compute": "fwd bf16 matrix core; bwd fp16 matrix core (dO and dS scaled by powers of two); "
+                   "fp32 accumulation and softmax",
+        "kernel_timing": "kernels: HIP events around a replayed HIP graph of `steps` back-to-back "
+                         "launches of each; ms_per_step: the plain loop of `steps` steps; "
+                         "ms_per_step_graph: a replayed graph of `steps` steps",
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -415,6 +527,76 @@ def main():
                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)},
                        "bwd_ms": round(ms_bwd_rope, 5), "bwd_plain_ms": round(bwd_ms, 5)}
+    # The measured matrix-core peak (calibration kernel, the way the pages measure theirs):
+    # one wave of workgroups (2 per CU, 8 waves per CU), every wave 4 independent chains of
+    # 32x32x16 bf16 products on registers; HIP events around one launch; the kernel's own
+    # shader-clock / 100 MHz counter ratio gives the clock the matrix cores ran at.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    cb, ci = 2 * cus, 8192
+    c_sink = torch.empty(cb * 256, dtype=torch.float32, device="cuda")
+    c_clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    def calib():
+        return cg.calib_mfma(cb, ci, stream=stream, sink=c_sink, clocks=c_clk)[2]
+    for _ in range(3):
+        calib_flops = calib()
+    ms_calib = timed(calib, 4)
+    assert bool((c_sink == ci / 64.0).all()), "calibration products are off"
+    clk = c_clk.cpu().tolist()
+    peak_meas = calib_flops / (ms_calib * 1e-3) / 1e12
+    out["mfma_measured_peak"] = {
+        "tflops": round(peak_meas, 1), "frac_of_spec": round(peak_meas / PEAK_BF16_TFLOPS, 4),
+        "clock_ghz": round(clk[0] / (clk[1] * 1e-8) / 1e9, 3) if clk[1] else None,
+        "method": f"cgqa_calib_mfma: {cb} workgroups x 4 waves (one wave of workgroups on {cus} CUs), "
+                  f"4 independent chains of {ci} v_mfma_f32_32x32x16_bf16 per wave, no memory traffic; "
+                  f"HIP events around one launch, median of {args.repeats}"}
+    for name in kernels:
+        kernels[name]["frac_measured_peak"] = round(kernels[name]["tflops"] / peak_meas, 4)
+    out["roofline"]["frac_measured_peak"] = round(achieved / peak_meas, 4)
+    out["fwdbwd_pct_measured_peak"] = round(100 * value / peak_meas, 2)
+    del c_sink, c_clk
+
+    if not args.no_configs:
+        # Every workload: each kernel's share of a step as above, but from replays of captured
+        # HIP graphs (the small workloads' kernels are shorter than their host dispatch);
+        # credited flops per causal pair as above, against the spec and the measured peak.
+        cfgs = {}
+        for wi, wk in enumerate(si.WORKLOADS):
+            xw = si.make_workload_inputs(wk, seed=wi + 1)
+            dw = {n: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for n, a in xw.items()}
+            del xw
+            ow = torch.empty_like(dw["q"])
+            lw = torch.empty((wk.B, wk.Hq, wk.T), dtype=torch.float32, device="cuda")
+            dlw = cg.bwd_delta(wk.B, wk.Hq, wk.T, device="cuda")
+            dqw = torch.empty((wk.B, wk.T, wk.Hq, wk.d), dtype=torch.float32, device="cuda")
+            dkw = torch.empty((wk.B, wk.T, wk.Hkv, wk.d), dtype=torch.float32, device="cuda")
+            dvw = torch.empty_like(dkw)
+            # (launched on the current stream, which graph capture switches)
+            fns = (lambda: cg.attn_fwd(dw["q"], dw["k"], dw["v"], scale=wk.scale, o=ow, lse=lw),
+                   lambda: cg.attn_bwd_dq(dw["q"], dw["k"], dw["v"], ow, dw["do"], lw, scale=wk.scale,
+                                          delta=dlw, dq=dqw),
+                   lambda: cg.attn_bwd_dkv(dw["q"], dw["k"], dw["v"], dw["do"], lw, dlw, scale=wk.scale,
+                                           dk=dkw, dv=dvw))
+            n = 10 if wk.d * wk.causal_pairs > 5e10 else args.steps
+            for _ in range(3):
+                for fn in fns:
+                    fn()
+            torch.cuda.synchronize()
+            ms3 = [graph_timed(fn, n) for fn in fns]
+            st_ms = graph_timed(lambda: [fn() for fn in fns], n)
+            entry = {"steps": n}
+            for name, ms_, per_pair in zip(("attn_fwd", "attn_bwd_dq", "attn_bwd_dkv"), ms3, (4, 6, 8)):
+                tf = per_pair * wk.d * wk.causal_pairs / (ms_ * 1e-3) / 1e12
+                entry[name] = {"ms": round(ms_, 5), "tflops": round(tf, 1),
+                               "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                               "pct_measured_peak": round(100 * tf / peak_meas, 2)}
+            st_tf = 14 * wk.d * wk.causal_pairs / (st_ms * 1e-3) / 1e12
+            entry["step"] = {"ms": round(st_ms, 5), "tflops": round(st_tf, 1),
+                             "pct_peak": round(100 * st_tf / PEAK_BF16_TFLOPS, 2)}
+            cfgs[wk.name] = entry
+            del dw, ow, lw, dlw, dqw, dkw, dvw, fns
+            torch.cuda.empty_cache()
+        out["configs"] = cfgs
+
     if graph_failures:
         out["graph_capture_failed"] = graph_failures   # these were timed call by call instead
     if not args.no_cpu:

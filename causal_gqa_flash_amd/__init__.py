@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     attn_naive_workspace_bytes,
     attn_status_string,
     bwd_delta,
+    calib_mfma,
     gemm,
     gemm_workspace_bytes,
     library,

@@ -68,6 +68,8 @@ def library():
         lib.attn_bwd_dq_rope.restype = i
         lib.attn_bwd_dkv_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.attn_bwd_dkv_rope.restype = i
+        lib.cgqa_calib_mfma.argtypes = [vp, vp, i, i, ctypes.POINTER(ctypes.c_double), vp]
+        lib.cgqa_calib_mfma.restype = i
         lib.cgqa_gemm_static.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
         lib.cgqa_gemm_static.restype = i
         lib.cgqa_gemm_workspace_bytes.argtypes = [i, i, i]
@@ -417,3 +419,22 @@ def rope_qk(q, k, cos, sin, q_out=None, k_out=None, stream=None):
         _ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(cos), _ptr(sin), B, T, Hq, Hkv, d,
         rq, rk, rqo, rko, _stream_ptr(stream)))
     return q_out, k_out
+
+
+def calib_mfma(blocks, iters, stream=None, sink=None, clocks=None):
+    """Launches the matrix-core calibration (cgqa_calib_mfma): returns the device sink
+    (blocks*256 fp32, each iters/64), the device clocks (int64 [2]: block 0's loop in shader
+    clocks and in 100 MHz ticks) and the launch's flop count. sink and clocks may be given
+    (to launch without allocating)."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    if clocks is None:
+        clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    _need(sink, "sink", torch.float32, (blocks * 256,))
+    _need(clocks, "clocks", torch.int64, (2,))
+    flops = ctypes.c_double(0.0)
+    _check("cgqa_calib_mfma", library().cgqa_calib_mfma(_ptr(sink), _ptr(clocks), blocks, iters,
+                                                        ctypes.byref(flops), _stream_ptr(stream)))
+    return sink, clocks, flops.value
+

@@ -6,7 +6,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcgqa.so")
-SOURCES = ["api.hip", "attn_fwd.hip", "attn_fwd_par.hip", "attn_bwd.hip", "attn_naive.hip", "gemm.hip", "rope.hip"]
+SOURCES = ["api.hip", "attn_fwd.hip", "attn_fwd_par.hip", "attn_bwd.hip", "attn_naive.hip", "gemm.hip", "rope.hip",
+           "calib.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for all device code; the host pass

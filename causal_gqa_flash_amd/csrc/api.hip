@@ -355,6 +355,19 @@ int cgqa_gemm(const uint16_t* A, const uint16_t* B, void* C, const float* R, int
     return gemm_impl(A, B, C, R, M, N, K, flags, workspace, workspace_bytes, stream);
 }
 
+int cgqa_calib_mfma(float* sink, uint64_t* clocks, int blocks, int iters, double* flops, void* stream) {
+    if (blocks < 1 || blocks > (1 << 16) || iters < 1 || iters > (1 << 20)) return CGQA_EINVAL;
+    if (!sink) return CGQA_EINVAL;
+    if (!aligned16(sink) || (clocks && !aligned16(clocks))) return CGQA_EUNSUPPORTED;
+    if (clocks) {
+        const int64_t n = (int64_t)blocks * cgqa::kCalibThreads;
+        if (!disjoint(View{sink, 1, n, n, 4}, View{clocks, 1, 2, 2, 8})) return CGQA_EINVAL;
+    }
+    if (flops) *flops = cgqa::calib_mfma_flops(blocks, iters);
+    return finish(cgqa::launch_calib_mfma(sink, reinterpret_cast<unsigned long long*>(clocks), blocks, iters,
+                                          (hipStream_t)stream));
+}
+
 static_assert(cgqa::kGemmScratchBytes == CGQA_GEMM_STATIC_SCRATCH_BYTES, "scratch size");
 
 int cgqa_gemm_static(const uint16_t* A, const uint16_t* B, void* C, const float* R, int M, int N, int K,

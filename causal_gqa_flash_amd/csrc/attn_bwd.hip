@@ -502,7 +502,9 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     // keeping it in a register: the loop sits at the register budget of three waves per
     // SIMD, and one more live value there makes the compiler trade the products'
     // overlap with the softmax for register pressure (measured: about 7% slower).
-    auto load_sigma = [&]() CGQA_INLINE { return sigma_sh; };
+    auto load_sigma = [&]() CGQA_INLINE {
+        return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(sigma_sh)));   // uniform: a scalar
+    };
     // Raw step -> converted step (fp16 rows, scaled and masked statistics).
     auto convert_step = [&](int st, float sigma) CGQA_INLINE {
         const char* raw = slot_base + cvt_cur.stage * C::kRawStage;
@@ -740,7 +742,8 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
             }
         }
     };
-    const float sigma_inv = 1.0f / load_sigma();   // exact: a power of two
+    // 1 / sigma for a power of two 2^k (k in [-126, 126]): exponent field 254 - that of sigma
+    const float sigma_inv = __uint_as_float((254u << 23) - __float_as_uint(load_sigma()));
     reduce_store(dkacc, a.dk, a.scale * sigma_inv, std::integral_constant<bool, ROPE>{});
     reduce_store(dvacc, a.dv, sigma_inv, std::false_type{});
 }

@@ -23,6 +23,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -96,15 +97,16 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16(const u32x4& w) {
 __device__ __forceinline__ u32x4 bf16x8_to_f16_bits(const u32x4& w) {
     return __builtin_bit_cast(u32x4, bf16x8_to_f16(w));
 }
-// The same values times a power of two `s` (exact in fp32) before the fp16 rounding.
+// The same values times a power of two `s` (exact in fp32) before the fp16 rounding,
+// one pair at a time (two fp32 temporaries live at once).
 __device__ __forceinline__ u32x4 bf16x8_to_f16_bits_scaled(const u32x4& w, float s) {
-    f32x8 f;
+    u32x4 out;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __builtin_bit_cast(float, w[i] << 16) * s;
-        f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u) * s;
+        const f32x2 f = {__builtin_bit_cast(float, w[i] << 16) * s, __builtin_bit_cast(float, w[i] & 0xFFFF0000u) * s};
+        out[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
     }
-    return __builtin_bit_cast(u32x4, __builtin_convertvector(f, f16x8));
+    return out;
 }
 
 // Eight accumulator registers (base .. base+7) rounded to bf16 (round to nearest

@@ -83,6 +83,12 @@ struct GemmArgs {
 };
 // Splits of K the launcher uses for this shape and workspace size (1: none).
 int gemm_splits(int M, int N, int K, size_t ws_bytes);
+// Matrix-core calibration (calib.hip): `blocks` workgroups of kCalibThreads threads; each
+// thread stores iters / 64 to sink[block * kCalibThreads + thread]; clocks (or null) gets
+// block 0's loop time in shader clocks and in 100 MHz ticks.
+constexpr int kCalibThreads = 256;
+hipError_t launch_calib_mfma(float* sink, unsigned long long* clocks, int blocks, int iters, hipStream_t stream);
+double calib_mfma_flops(int blocks, int iters);
 // Bytes of the static split-K scratch of the allocation-free GEMM (per device), and its
 // device address on the current device (looked up once per device).
 constexpr size_t kGemmScratchBytes = (size_t)16 << 20;

@@ -262,6 +262,19 @@ int cgqa_gemm(const uint16_t* A, const uint16_t* B, void* C, const float* R,
 int cgqa_gemm_static(const uint16_t* A, const uint16_t* B, void* C, const float* R,
                      int M, int N, int K, int flags, void* stream);
 
+/* Calibration, not attention: the rate the matrix core reaches on this GPU, so kernels can
+ * be reported against a measured peak beside the spec sheet's (page "Talking to the GPU",
+ * section "The real tensor core peak", times a kernel that only does tensor-core products).
+ * Runs `blocks` workgroups of 256 threads; each wave issues 4 independent chains of `iters`
+ * 32x32x16 bf16 matrix products on register operands (all 1/64) and each thread stores
+ * iters / 64 (exact) to sink[block * 256 + thread] (device memory of blocks * 256 floats,
+ * 16-byte aligned). clocks, if not null (device memory of 2 values, 16-byte aligned), gets
+ * block 0's loop time as shader clocks and as ticks of the constant 100 MHz counter, whose
+ * ratio is the clock the matrix cores ran at. *flops, if not null (host memory), receives
+ * the flop count of the launch (2 flops per multiply-add); its time comes from the caller's
+ * events. 1 <= blocks <= 65536, 1 <= iters <= 2^20, else CGQA_EINVAL. */
+int cgqa_calib_mfma(float* sink, uint64_t* clocks, int blocks, int iters, double* flops, void* stream);
+
 /* Static description of a return code (never NULL): every call reports failure as a code
  * whose meaning can be printed, the library-side form of the pages' practice of naming each
  * failed call and the error behind it (page "Talking to the GPU", section "One macro for

@@ -439,3 +439,14 @@ def test_gemm_static_rejects_shapes_beyond_its_scratch():
     assert lib.cgqa_gemm_static(*p, 256, 384, 100, 0, None) == cg.CGQA_EUNSUPPORTED   # K % 32
     assert lib.cgqa_gemm_static(p[0], p[1], None, None, 256, 384, 8192, 0, None) == cg.CGQA_EINVAL
     assert lib.cgqa_gemm_static(*p, 0, 384, 8192, 0, None) == cg.CGQA_OK             # empty
+
+
+def test_calib_rejections():
+    lib = cg.library()
+    s, c = fake(0), fake(1)
+    for blocks, iters in ((0, 10), (1 << 17, 10), (4, 0), (4, (1 << 20) + 1)):
+        assert lib.cgqa_calib_mfma(s, c, blocks, iters, None, None) == cg.CGQA_EINVAL
+    assert lib.cgqa_calib_mfma(None, c, 4, 10, None, None) == cg.CGQA_EINVAL
+    assert lib.cgqa_calib_mfma(s + 8, c, 4, 10, None, None) == cg.CGQA_EUNSUPPORTED
+    assert lib.cgqa_calib_mfma(s, c + 8, 4, 10, None, None) == cg.CGQA_EUNSUPPORTED
+    assert lib.cgqa_calib_mfma(s, s + 64, 4, 10, None, None) == cg.CGQA_EINVAL   # clocks inside sink
