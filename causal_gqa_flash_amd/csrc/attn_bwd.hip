@@ -770,8 +770,7 @@ struct DqPipeCfg {
     static constexpr int kRawStage = 2 * kTile;      // K then V
     static constexpr int kDepth = 4;
     static constexpr int kRaw = kDepth * kRawStage;
-    static constexpr int kPitch = 2 * D + 16;        // fp16 K rows, padded
-    static constexpr int kHalfTile = 32 * kPitch;
+    static constexpr int kHalfTile = 32 * kRow;      // fp16 K of a block (swizzled chunks, as the raw tiles)
     static constexpr int kLds = kRaw + kDepth * kHalfTile;
     static constexpr int kChunks = kTile / 1024;     // 1 KB DMA chunks per tensor
     static constexpr int kRowsPerChunk = 1024 / kRow;
@@ -887,19 +886,31 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
 
     // Per-lane LDS addresses. A operand rows (raw tile): row n, logical chunk 2kd + hl.
     // Transposing reads of fp16 K: rows 16tt + 4hl + (lane&15)/4 (+8), columns
-    // 32mb + 16((lane>>4)&1) + 4(lane&3).
+    // 32mb + 16((lane>>4)&1) + 4(lane&3), i.e. logical chunk 4mb + 2((lane>>4)&1) +
+    // (lane&3)/2, 8 bytes in. The fp16 tile has the raw tiles' chunk swizzle (a padded
+    // pitch lets the four rows of a transposing read meet in the same banks); rows enter
+    // it through r % 16, so 16tt is an immediate.
     const char* aaddr[C::kKD];
     {
         const int swz = chunk_swizzle<D>(n);
 #pragma unroll
         for (int kd = 0; kd < C::kKD; ++kd) aaddr[kd] = raw + n * C::kRow + (((2 * kd + hl) ^ swz) << 4);
     }
-    const char* traddr = k16 + (4 * hl + ((lane & 15) >> 2)) * C::kPitch +
-                         2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    const char* traddr[C::kMB][2];
+    {
+        const int r0 = 4 * hl + ((lane & 15) >> 2);
+        const int chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+        for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                traddr[mb][r] = k16 + (r0 + 8 * r) * C::kRow + 8 * (lane & 1) +
+                                (((4 * mb + chunk) ^ chunk_swizzle<D>(r0 + 8 * r)) << 4);
+    }
     // Conversion of a raw K block to fp16: thread tid takes row tid/8, logical chunk tid%8.
     const int cv_r = tid / (C::kRow / 16), cv_c = tid % (C::kRow / 16);
     const char* cv_src = raw + cv_r * C::kRow + ((cv_c ^ chunk_swizzle<D>(cv_r)) << 4);
-    char* cv_dst = k16 + cv_r * C::kPitch + cv_c * 16;
+    char* cv_dst = k16 + cv_r * C::kRow + ((cv_c ^ chunk_swizzle<D>(cv_r)) << 4);
 
     // (ALWAYS: the caller knows block t+1 exists.)
     auto sync_and_stage = [&](int t, int iss, int rst, int cst, auto Ac) {
@@ -956,8 +967,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
         for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
             for (int mb = 0; mb < C::kMB; ++mb) {
-                const char* p0 = traddr + cst * C::kHalfTile + 16 * tt * C::kPitch + 64 * mb;
-                const f16x8 kt = concat(lds_read_tr4_f16(p0), lds_read_tr4_f16(p0 + 8 * C::kPitch));
+                const int off = cst * C::kHalfTile + 16 * tt * C::kRow;
+                const f16x8 kt = concat(lds_read_tr4_f16(traddr[mb][0] + off), lds_read_tr4_f16(traddr[mb][1] + off));
                 dqacc[mb] = mfma32x32x16(kt, dk[tt], dqacc[mb]);
                 kbar[mb] = mfma32x32x16(kt, pk[tt], kbar[mb]);
             }

@@ -298,8 +298,9 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_par_kernel(FwdA
     using Tr = std::true_type;
 
     // ---- the wave's stages 0 .. my_len-1 (step -1 computes the first scores). Every wave
-    // joins the barrier of every step -1 .. nsteps-1.
-    sync(-1);
+    // joins the barrier of every step -1 .. nsteps-1. Batches -2 and -1 went out before Q,
+    // whose loads the compiler waited for, so step -1 only needs the barrier.
+    wait_tiles_barrier<0>();
     int s_next = 0;
     if (my_len > 0) {
         scores(koff(0), s_cur);
