@@ -505,30 +505,46 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     auto load_sigma = [&]() CGQA_INLINE {
         return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(sigma_sh)));   // uniform: a scalar
     };
-    // Raw step -> converted step (fp16 rows, scaled and masked statistics).
-    auto convert_step = [&](int st, float sigma) CGQA_INLINE {
+    // Raw step -> converted step (fp16 rows, scaled and masked statistics). `idle` is the
+    // set of the slot's waves (bit kwr) that have no products in the current step: when
+    // there are some, they do the whole conversion between them and the waves with
+    // products skip it; otherwise every thread of the slot converts its share. (A slot's
+    // late key blocks wait for most of the stream before their diagonal comes.) Both
+    // ways give the same bits. At d = 128 (one wave per SIMD at 256 registers) the extra
+    // path made the loop slower; there every thread converts its share.
+    constexpr bool kIdleConvert = D == 64;
+    auto convert_chunk = [&](const char* raw, char* cv, int t, int ch, float sigma) CGQA_INLINE {
+        const int row = ch / (C::kRawRow / 16), col = ch % (C::kRawRow / 16);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(raw + t * C::kRawTile + ch * 16);
+        store16(cv + t * C::kTile + row * C::kPitch + col * 16,
+                t == 0 ? bf16x8_to_f16_bits(x) : bf16x8_to_f16_bits_scaled(x, sigma));
+    };
+    auto convert_stat = [&](const char* raw, char* cv, int i, int qs0, float sigma) CGQA_INLINE {
+        const float x = reinterpret_cast<const float*>(raw + 2 * C::kRawTile)[i];
+        const bool valid = qs0 + (i % BQ) < T;
+        float y;
+        if (i < BQ) y = valid ? x * kLog2e : INFINITY;    // P = 0 past T
+        else y = valid ? x * sigma : 0.0f;
+        reinterpret_cast<float*>(cv + 2 * C::kTile)[i] = y;
+    };
+    auto convert_step = [&](int st, float sigma, unsigned idle) CGQA_INLINE {
         const char* raw = slot_base + cvt_cur.stage * C::kRawStage;
         char* cv = conv_stage(st);
         const int qs0 = cvt_cur.q0;
         advance(cvt_cur);
+        if (!kIdleConvert || idle == 0) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int i = 0; i < C::kConvChunks; ++i) {
-                const int ch = stid + i * C::kSlotThreads;
-                const int row = ch / (C::kRawRow / 16), col = ch % (C::kRawRow / 16);
-                const u32x4 x = *reinterpret_cast<const u32x4*>(raw + t * C::kRawTile + ch * 16);
-                store16(cv + t * C::kTile + row * C::kPitch + col * 16,
-                        t == 0 ? bf16x8_to_f16_bits(x) : bf16x8_to_f16_bits_scaled(x, sigma));
-            }
-        }
-        if (stid < 2 * BQ) {
-            const float x = reinterpret_cast<const float*>(raw + 2 * C::kRawTile)[stid];
-            const bool valid = qs0 + (stid % BQ) < T;
-            float y;
-            if (stid < BQ) y = valid ? x * kLog2e : INFINITY;    // P = 0 past T
-            else y = valid ? x * sigma : 0.0f;
-            reinterpret_cast<float*>(cv + 2 * C::kTile)[stid] = y;
+                for (int i = 0; i < C::kConvChunks; ++i) convert_chunk(raw, cv, t, stid + i * C::kSlotThreads, sigma);
+            if (stid < 2 * BQ) convert_stat(raw, cv, stid, qs0, sigma);
+        } else if (idle >> kwr & 1u) {
+            constexpr int kPerTensor = C::kRawTile / 16;
+            const int nid = __builtin_popcount(idle);
+            const int rank = __builtin_popcount(idle & ((1u << kwr) - 1u));
+            for (int ch = 64 * rank + lane; ch < kPerTensor; ch += 64 * nid) convert_chunk(raw, cv, 0, ch, sigma);
+            for (int ch = 64 * rank + lane; ch < kPerTensor; ch += 64 * nid) convert_chunk(raw, cv, 1, ch, sigma);
+            if (rank == 0 && lane < 2 * BQ) convert_stat(raw, cv, lane, qs0, sigma);
         }
     };
     auto wait_barrier = [&](int pending_steps) CGQA_INLINE {
@@ -584,7 +600,7 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
         const float sigma = pow2_normalizer(__builtin_amdgcn_readfirstlane(m)).s;
         if (tid == 0) sigma_sh = sigma;      // read in the loop, after its first barrier
         for (int st = 1; st < NR && st < nsteps; ++st) issue_step();
-        if (nsteps > 0) convert_step(0, sigma);
+        if (nsteps > 0) convert_step(0, sigma, 0u);
     }
 
     const int tr_row = (lane & 15) >> 2;
@@ -647,8 +663,8 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
         wait_barrier(min(step + NR - 1, nsteps - 1) - (step + 1));
         if (step + NR < nsteps) issue_step();
     };
-    auto convert_next = [&](int step) CGQA_INLINE {
-        if (step + 1 < nsteps) convert_step(step + 1, load_sigma());
+    auto convert_next = [&](int step, unsigned idle) CGQA_INLINE {
+        if (step + 1 < nsteps) convert_step(step + 1, load_sigma(), idle);
     };
     auto compute_step = [&](auto Mc, int step) CGQA_INLINE {
         const char* qs = conv_stage(step);
@@ -660,24 +676,38 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     // that precede all its keys: loads and conversions only), the diagonal step (with
     // the mask), then the rest. Waves without a block only keep the loads going.
     const int diag = kwb < T ? kwb / 32 - qt_begin : per_head;   // diagonal step within a pass
+    // The diagonal steps of the slot's waves (wave kwr of slot hs holds position
+    // (kwr + hs) % NKW): wave k has no products in the steps of a pass before its own.
+    int slot_diag[NKW];
+#pragma unroll
+    for (int k = 0; k < NKW; ++k) {
+        const int gpk = p0 + (k + hs) % NKW;
+        slot_diag[k] = gpk < nkb ? block_at(gpk) - qt_begin : per_head;
+    }
+    auto idle_at = [&](int r) CGQA_INLINE {   // r: step within the pass
+        unsigned m = 0;
+#pragma unroll
+        for (int k = 0; k < NKW; ++k) m |= (r < slot_diag[k] ? 1u : 0u) << k;
+        return m;
+    };
     for (int hp = 0; hp < heads_per_slot; ++hp) {
         const int s0 = hp * per_head, s1 = s0 + per_head;
         const int sd = min(s0 + diag, s1);
         int step = s0;
         for (; step < sd; ++step) {
             sync_step(step);
-            convert_next(step);
+            convert_next(step, idle_at(step - s0));
         }
         if (step < s1) {
             sync_step(step);
             compute_step(std::true_type{}, step);
-            convert_next(step);
+            convert_next(step, idle_at(step - s0));
             ++step;
         }
         for (; step < s1; ++step) {
             sync_step(step);
             compute_step(std::false_type{}, step);
-            convert_next(step);
+            convert_next(step, idle_at(step - s0));
         }
     }
     lds_barrier();
