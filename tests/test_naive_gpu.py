@@ -11,10 +11,15 @@ from parity_util import LSE_ABS, MAX_ABS, REL_L2, compare, oracle_run, to_device
 
 pytestmark = pytest.mark.gpu
 
-# (B, T, Hq, Hkv, d, seed): the pages' awkward gradient-check sizes (head 12, four query
-# heads on two kv heads), single token, ragged tails, G = 1 .. 8, odd head dimensions.
-SHAPES = [(3, 9, 4, 2, 12, 41), (1, 1, 6, 2, 64, 42), (2, 33, 6, 2, 64, 43), (1, 100, 8, 2, 128, 44),
-          (2, 65, 3, 1, 32, 45), (1, 130, 8, 1, 96, 46), (1, 77, 8, 8, 64, 47)]
+# (B, T, Hq, Hkv, d, seed, qk_mult): the pages' awkward gradient-check sizes (head 12,
+# four query heads on two kv heads), single token, ragged tails, G = 1 .. 8, odd head
+# dimensions; then sequences as long as one (batch, kv head) slice of the larger workloads
+# (T = 1024 and 2048, d = 128, and a peaky softmax), so that the full-size comparisons
+# below rest on a naive mode pinned at those lengths too.
+SHAPES = [(3, 9, 4, 2, 12, 41, 1.0), (1, 1, 6, 2, 64, 42, 1.0), (2, 33, 6, 2, 64, 43, 1.0),
+          (1, 100, 8, 2, 128, 44, 1.0), (2, 65, 3, 1, 32, 45, 1.0), (1, 130, 8, 1, 96, 46, 1.0),
+          (1, 77, 8, 8, 64, 47, 1.0), (1, 1024, 6, 2, 64, 49, 1.0), (1, 2048, 3, 1, 64, 50, 2.0),
+          (1, 1024, 4, 1, 128, 51, 1.0)]
 
 
 def _naive(x, scale, B, T, Hq, Hkv, d):
@@ -28,20 +33,22 @@ def _naive(x, scale, B, T, Hq, Hkv, d):
     return {n: t.float().cpu().numpy().astype(np.float64) for n, t in out.items()}, dev
 
 
-# Naive against the oracle. The naive kernels compute in fp32 with sums of at most a few
-# hundred terms here, so they agree with fp64 to ~1e-6 relative; o is then rounded to
-# bf16, whose unit roundoff is 2^-8 (8 significant bits, round to nearest).
+# Naive against the oracle. The naive kernels compute in fp32 with sums of at most 2048
+# terms here (recursive fp32 sums err by at most n * 2^-24 relative, 1.2e-4 at n = 2048 in
+# the worst case and about sqrt(n) * 2^-24 typically), so they agree with fp64 well inside
+# 1e-4 relative; o is then rounded to bf16, whose unit roundoff is 2^-8 (8 significant
+# bits, round to nearest).
 def _close(name, got, want, rel, atol):
     err = np.abs(got - want)
     bound = atol + rel * np.abs(want)
     assert np.all(err <= bound), (name, tuple(np.argwhere(err > bound)[0]), float(err.max()))
 
 
-@pytest.mark.parametrize("B,T,Hq,Hkv,d,seed", SHAPES)
-def test_naive_matches_oracle(B, T, Hq, Hkv, d, seed):
-    print(f"naive vs oracle B={B} T={T} Hq={Hq} Hkv={Hkv} d={d} seed={seed}", flush=True)
+@pytest.mark.parametrize("B,T,Hq,Hkv,d,seed,mult", SHAPES)
+def test_naive_matches_oracle(B, T, Hq, Hkv, d, seed, mult):
+    print(f"naive vs oracle B={B} T={T} Hq={Hq} Hkv={Hkv} d={d} seed={seed} mult={mult}", flush=True)
     scale = 1.0 / np.sqrt(d)
-    x = si.make_inputs(B, T, Hq, Hkv, d, seed, 1.0)
+    x = si.make_inputs(B, T, Hq, Hkv, d, seed, mult)
     got, _ = _naive(x, scale, B, T, Hq, Hkv, d)
     want = oracle_run(x, scale)
     _close("o", got["o"], want["o"], 2.0 ** -8 + 1e-5, 1e-6)

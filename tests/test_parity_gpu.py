@@ -58,8 +58,10 @@ def test_parity_small(B, T, Hq, Hkv, d, seed, mult):
 
 @pytest.mark.parametrize("w", si.WORKLOADS, ids=[w.name for w in si.WORKLOADS])
 def test_parity_full_workload(w):
-    """Full-size launch; the oracle checks the first and the last (batch, kv head) slice
-    (and the whole problem for the two smallest workloads)."""
+    """Full-size launch; the oracle checks (batch, kv head) slices spread evenly over the
+    launch, first and last included: eight at d = 64, four at d = 128 (and the whole problem
+    for the two smallest workloads). Slices are independent, so each is the oracle's full
+    answer for its rows; they sit at different grid positions, XCDs and tile orders."""
     _log(f"parity full {w.name}")
     x = si.make_workload_inputs(w, seed=si.WORKLOADS.index(w) + 1)
     got = gpu_run(x, w.scale)
@@ -68,7 +70,12 @@ def test_parity_full_workload(w):
         ok, msg = check_all(got, want)
         assert ok, msg
         return
-    for b, g in ((0, 0), (w.B - 1, w.Hkv - 1)):
+    n_slices = w.B * w.Hkv
+    k = 8 if w.d == 64 else 4
+    picks = sorted({round(i * (n_slices - 1) / (k - 1)) for i in range(k)})
+    for p in picks:
+        b, g = divmod(p, w.Hkv)
+        _log(f"  slice b={b} g={g}")
         xs = si.slice_group(x, w.Hq, w.Hkv, b, g)
         want = oracle_run(xs, w.scale)
         ok, msg = check_all(slice_outputs(got, w.Hq, w.Hkv, b, g), want)
