@@ -349,7 +349,10 @@ struct DkvCfg {
     static constexpr int kSlotThreads = NKW * 64;
     static constexpr int kTileLoads = kRawTile / 1024 / NKW;     // per tensor, per wave
     static constexpr int kStatLanes = 2 * BQ / NKW;              // 4-byte DMA lanes per wave
-    static constexpr int kVmPerStep = 2 * kTileLoads + 1;        // DMA instructions per wave
+    // A slot of one wave loads lse and delta itself: two 4-byte loads, each under half of
+    // the lanes (a load's base is wave-uniform).
+    static constexpr int kStatLoads = kStatLanes > BQ ? 2 : 1;
+    static constexpr int kVmPerStep = 2 * kTileLoads + kStatLoads;   // DMA instructions per wave
     static constexpr int kConvChunks = kRawTile / 16 / kSlotThreads;   // per tensor, per thread
     // Reduction area: one 32-dim accumulator block (16 floats) per lane of every wave
     // of slots 1 .. HS-1; the blocks are reduced one after another.
@@ -490,7 +493,12 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
             load_lds16_chunks<1>(a.q + dma_cur.row, o1, lds + 1024 * i);
             load_lds16_chunks<1>(a.dO + (SAME_QDO ? dma_cur.row : dma_cur.row_do), o2, lds + C::kRawTile + 1024 * i);
         }
-        if (lane < C::kStatLanes) {
+        if constexpr (C::kStatLoads == 2) {
+            // Lanes 0 .. BQ-1 take lse, the others delta; both halves are always active.
+            const unsigned so = (unsigned)min(stat_row, last) * 4u, sd = raw + 2 * C::kRawTile;
+            if (lane < BQ) load_lds4_off(a.lse + dma_cur.stat, so, sd);
+            else load_lds4_off(a.delta + dma_cur.stat, so, sd);
+        } else if (lane < C::kStatLanes) {
             const float* sb = (stat_lse ? a.lse : a.delta) + dma_cur.stat;
             load_lds4_off(sb, (unsigned)min(stat_row, last) * 4u, raw + 2 * C::kRawTile + kwr * C::kStatLanes * 4);
         }
@@ -1125,7 +1133,15 @@ hipError_t launch_bwd_dkv(const BwdArgs& a, hipStream_t stream) {
     const int G = a.Hq / a.Hkv;
     if (a.d == 64) {
         if (G % 4 == 0) return launch_dkv_t<64, 32, 2, 4, 2>(a, stream);
-        if (G % 3 == 0) return launch_dkv_t<64, 32, 4, 3, 3>(a, stream);
+        if (G % 3 == 0) {
+            // Tiny grids (at most 32 workgroups of four key blocks) take one key block per
+            // workgroup: four times the workgroups on an idle chip (B1 T64 Hq6 Hkv2: 9.1 ->
+            // 7.2 us). Larger ones keep four: a single wave's step is no faster alone (B8
+            // T512: 28.9 -> 30.5 us with one block per workgroup).
+            const long nkb = (a.T + 31) / 32;
+            if ((long)a.B * a.Hkv * ((nkb + 3) / 4) <= 32) return launch_dkv_t<64, 32, 1, 3, 3>(a, stream);
+            return launch_dkv_t<64, 32, 4, 3, 3>(a, stream);
+        }
         if (G % 2 == 0) return launch_dkv_t<64, 32, 4, 2, 3>(a, stream);
         return launch_dkv_t<64, 32, 4, 1, 3>(a, stream);
     }

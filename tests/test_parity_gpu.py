@@ -42,6 +42,11 @@ SMALL = [
     (4, 150, 6, 2, 64, 18, 1.0),
     (8, 45, 4, 2, 64, 19, 2.0),
     (2, 333, 12, 4, 64, 20, 1.0),
+    # G divisible by 3 takes one key block per dK/dV workgroup on tiny grids (at most 32
+    # workgroups of four blocks: every shape above) and four blocks otherwise: ragged
+    # shapes just past that size run the four-block dealing with its zig-zag order
+    (17, 100, 6, 2, 64, 22, 1.0),
+    (12, 300, 3, 1, 64, 23, 2.0),
 ]
 
 
