@@ -94,6 +94,7 @@ int fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* 
     a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
     a.q_rs = q_rs; a.kv_rs = kv_rs; a.o_rs = o_rs;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    a.div = cgqa::make_map_divs(B, Hq, Hkv);
     return finish(cgqa::launch_fwd(a, (hipStream_t)stream));
 }
 
@@ -173,6 +174,7 @@ int bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
     a.dq_rs = st.dq_rs; a.dkv_rs = st.dkv_rs; a.grad_bf16 = st.grad == CGQA_GRAD_BF16 ? 1 : 0;
     a.scale = scale;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    a.div = cgqa::make_map_divs(B, Hq, Hkv);
     return finish(is_dq ? cgqa::launch_bwd_dq(a, (hipStream_t)stream)
                         : cgqa::launch_bwd_dkv(a, (hipStream_t)stream));
 }

@@ -73,18 +73,22 @@ struct DqCfg {
 // fetches the slice's K and V from HBM).
 struct DqTile { int qt, b, h; };
 __device__ inline DqTile dq_tile(const BwdArgs& a, int bid) {
-    const int G = a.Hq / a.Hkv;
+    const int G = a.div.G;
     if (a.xcd_group) {
         const int xcd = bid & 7;
-        const int per_qt = ((a.B * a.Hkv) >> 3) * G;   // workgroups per query tile on one XCD
+        const int per_qt = a.div.tile.d;                 // workgroups per query tile on one XCD
         const int local = bid >> 3;
-        const int rem = local % per_qt;
-        const int p = xcd + 8 * (rem / G);               // slice b * Hkv + g
-        return {a.n_tiles - 1 - local / per_qt, p / a.Hkv, (p % a.Hkv) * G + rem % G};
+        const int jt = udiv(local, a.div.tile);
+        const int rem = local - jt * per_qt;
+        const int sl = udiv(rem, a.div.g);
+        const int p = xcd + 8 * sl;                      // slice b * Hkv + g
+        const int b = udiv(p, a.div.hkv);
+        return {a.n_tiles - 1 - jt, b, (p - b * a.Hkv) * G + (rem - sl * G)};
     }
-    const int bh_count = a.B * a.Hq;
-    const int bh = bid % bh_count;
-    return {a.n_tiles - 1 - bid / bh_count, bh / a.Hq, bh % a.Hq};
+    const int jt = udiv(bid, a.div.bhq);
+    const int bh = bid - jt * (a.B * a.Hq);
+    const int b = udiv(bh, a.div.hq);
+    return {a.n_tiles - 1 - jt, b, bh - b * a.Hq};
 }
 
 template <int D, int NQB, int BN, int NW>
@@ -92,10 +96,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     using C = DqCfg<D, NQB, BN, NW>;
     __shared__ __attribute__((aligned(16))) char smem[C::kLds];
 
-    const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
+    const int T = a.T, Hq = a.Hq;
     const DqTile wg = dq_tile(a, blockIdx.x);
     const int qt = wg.qt, b = wg.b, h = wg.h;
-    const int g = h / (Hq / Hkv);
+    const int g = udiv(h, a.div.g);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -380,12 +384,12 @@ __global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) 
     __shared__ float sigma_sh;                      // the dO scale (see below)
 
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
-    const int G = Hq / Hkv;
+    const int G = a.div.G;
     const int bg_count = a.B * Hkv;
     const int bid = blockIdx.x;
-    const int kt = bid / bg_count;                 // which group of block positions
-    const int bg = bid % bg_count;
-    const int b = bg / Hkv, g = bg % Hkv;
+    const int kt = udiv(bid, a.div.bhkv);          // which group of block positions
+    const int bg = bid - kt * bg_count;
+    const int b = udiv(bg, a.div.hkv), g = bg - b * Hkv;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -825,12 +829,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
 
     // Workgroup-uniform indices (readfirstlane keeps the integer divisions' results,
     // and everything derived from them, in scalar registers).
-    const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
+    const int T = a.T, Hq = a.Hq;
     const DqTile wg = dq_tile(a, blockIdx.x);
     const int qt = __builtin_amdgcn_readfirstlane(wg.qt);   // heaviest first
     const int b = __builtin_amdgcn_readfirstlane(wg.b);
     const int h = __builtin_amdgcn_readfirstlane(wg.h);
-    const int g = __builtin_amdgcn_readfirstlane(h / (Hq / Hkv));
+    const int g = __builtin_amdgcn_readfirstlane(udiv(h, a.div.g));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;

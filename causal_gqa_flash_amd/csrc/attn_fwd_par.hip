@@ -67,27 +67,30 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_par_kernel(FwdA
     __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
 
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
-    const int G = Hq / Hkv;
+    const int G = a.div.G;
     int qt, b, h;
     if (a.xcd_group) {
         // Slices p = b * Hkv + g with p % 8 == x % 8 run on XCD x % 8 (n_pairs % 8 == 0);
         // on each XCD the heaviest tiles are dispatched first.
         const int xcd = (int)blockIdx.x & 7;
-        const int per_qt = (a.n_pairs >> 3) * G;
+        const int per_qt = a.div.tile.d;   // (n_pairs / 8) * G
         const int local = (int)blockIdx.x >> 3;
-        qt = a.n_qtiles - 1 - local / per_qt;
-        const int rem = local % per_qt;
-        const int p = xcd + 8 * (rem / G);
-        b = p / Hkv;
-        h = (p % Hkv) * G + rem % G;
+        const int jt = udiv(local, a.div.tile);
+        qt = a.n_qtiles - 1 - jt;
+        const int rem = local - jt * per_qt;
+        const int sl = udiv(rem, a.div.g);
+        const int p = xcd + 8 * sl;
+        b = udiv(p, a.div.hkv);
+        h = (p - b * Hkv) * G + (rem - sl * G);
     } else {
         const int bh_count = a.B * Hq;
-        qt = a.n_qtiles - 1 - (int)blockIdx.x / bh_count;
-        const int bh = (int)blockIdx.x % bh_count;
-        b = bh / Hq;
-        h = bh % Hq;
+        const int jt = udiv((int)blockIdx.x, a.div.bhq);
+        qt = a.n_qtiles - 1 - jt;
+        const int bh = (int)blockIdx.x - jt * bh_count;
+        b = udiv(bh, a.div.hq);
+        h = bh - b * Hq;
     }
-    const int g = h / G;
+    const int g = udiv(h, a.div.g);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -10,6 +10,35 @@
 
 namespace cgqa {
 
+// Floor division by a divisor fixed at launch, on the scalar unit. For 0 <= n < 2^31 and
+// 1 <= d < 2^31, q0 = floor(n m / 2^32) with m = floor((2^32 - 1) / d) is floor(n / d) or
+// one less (n m / 2^32 lies in (n/d - 1, n/d]), and one comparison fixes it. The
+// compiler's general 32-bit division runs on the vector ALU (a float reciprocal, fix-ups and
+// readfirstlane) even for wave-uniform operands; this one stays in scalar registers.
+struct UDiv {
+    unsigned m;
+    int d;
+};
+inline UDiv make_udiv(int d) { return {0xFFFFFFFFu / (unsigned)d, d}; }
+__device__ __forceinline__ int udiv(int n, const UDiv& v) {
+    unsigned q = __umulhi((unsigned)n, v.m);
+    if ((unsigned)n - q * (unsigned)v.d >= (unsigned)v.d) ++q;
+    return (int)q;
+}
+// The divisors of the kernels' workgroup maps (set by the C-ABI layer before every launch):
+// G = Hq / Hkv; per-tile workgroups of one XCD ((B Hkv / 8) G when slices are grouped on
+// XCDs); B Hq; B Hkv.
+struct MapDivs {
+    int G;
+    UDiv g, hkv, hq, tile, bhq, bhkv;
+};
+inline MapDivs make_map_divs(int B, int Hq, int Hkv) {
+    const int G = Hq / Hkv;
+    const int tile = ((B * Hkv) >> 3) * G;
+    return {G, make_udiv(G), make_udiv(Hkv), make_udiv(Hq), make_udiv(tile > 0 ? tile : 1),
+            make_udiv(B * Hq), make_udiv(B * Hkv)};
+}
+
 struct FwdArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -22,6 +51,7 @@ struct FwdArgs {
     int n_qtiles;       // set by the launcher: query tiles per (batch, head)
     int n_pairs;        // set by the launcher: B * Hkv (batch, kv head) slices
     int xcd_group;      // set by the launcher: keep each slice's tiles on one XCD
+    MapDivs div;        // set by the C-ABI layer
 };
 
 struct BwdArgs {
@@ -47,6 +77,7 @@ struct BwdArgs {
     int n_tiles;        // set by the launcher
     int zigzag;         // dK/dV: deal key blocks in zig-zag order (set by the launcher)
     int xcd_group;      // dQ: keep each (batch, kv head) slice on one XCD (set by the launcher)
+    MapDivs div;        // set by the C-ABI layer
 };
 
 // Naive attention (attn_naive.hip): contiguous tensors, fp32 workspace p of B*Hq*T*T
