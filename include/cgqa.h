@@ -157,11 +157,13 @@ int attn_bwd_dkv_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v
  * fp32 [T][d/2], 16-byte aligned):
  *   y[2i] = x[2i] cos - x[2i+1] sin,   y[2i+1] = x[2i] sin + x[2i+1] cos.
  *
- * attn_rope_qk writes the rotated q and k as bf16 (computed in fp32, rounded to nearest
- * even); tensors are [B][T][H][d] with row strides as in the strided calls (multiples of
- * 8). An output may be its own input (same pointer and stride: in place, e.g. on the packed
- * QKV buffer); any other overlap of an output is CGQA_EINVAL. The forward then runs
- * attn_fwd on the rotated tensors.
+ * attn_rope_qk writes the rotated q and k as bf16, each value rounded to nearest (ties to
+ * even) from the exact rotated value (computed with one fp64 rounding, which decides every
+ * case but an exact value within 2^-53 relative of a bf16 tie without being one); tensors
+ * are [B][T][H][d] with row strides as in the strided calls (multiples of 8). An output
+ * may be its own input (same pointer and stride: in place, e.g. on the packed QKV buffer);
+ * any other overlap of an output is CGQA_EINVAL. The forward then runs attn_fwd on the
+ * rotated tensors.
  *
  * attn_bwd_dq_rope / attn_bwd_dkv_rope are attn_bwd_dq / attn_bwd_dkv on the rotated q and k
  * (contiguous, fp32 gradients) whose dq and dk are turned back inside the kernels, before
