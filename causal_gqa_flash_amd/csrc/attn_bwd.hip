@@ -92,7 +92,9 @@ __device__ inline DqTile dq_tile(const BwdArgs& a, int bid) {
 }
 
 template <int D, int NQB, int BN, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a_in) {
+    BwdArgs a = a_in;
+    pin_args(a);   // all argument loads at entry (see pin_args)
     using C = DqCfg<D, NQB, BN, NW>;
     __shared__ __attribute__((aligned(16))) char smem[C::kLds];
 
@@ -377,7 +379,20 @@ struct DkvCfg {
 // as bf16. ROPE: dK is turned back by the rotary tables. (Compile-time choices: run-time
 // ones cost this kernel registers it has not got.)
 template <int D, int BQ, int NKW, int HS, int NR, bool SAME_QDO, bool BF16OUT, bool ROPE>
-__global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NKW * HS * 64) void attn_bwd_dkv_kernel(BwdArgs a_in) {
+    BwdArgs a = a_in;
+    // d = 128: the arguments first used after the prologue are loaded at entry too (see
+    // pin_args; 3% faster at B4 T4096 Hq32). At d = 64 the same change moved the step
+    // loop's schedule and cost 4%, so there the compiler places those loads.
+    if constexpr (D == 128) {
+        pin_args(a.dO);
+        pin_args(a.lse);
+        pin_args(a.delta);
+        pin_args(a.do_absmax);
+        pin_args(a.dk);
+        pin_args(a.dv);
+        pin_args(a.dkv_rs);
+    }
     using C = DkvCfg<D, BQ, NKW, HS, NR>;
     __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
     __shared__ unsigned wg_red[C::kThreads / 64];   // one word per wave: the dO scale search
@@ -821,7 +836,9 @@ struct DqPipeCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_pipe_kernel(BwdArgs a_in) {
+    BwdArgs a = a_in;
+    pin_args(a);   // all argument loads at entry (see pin_args)
     using C = DqPipeCfg<D>;
     __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
     char* const raw = smem;

@@ -299,6 +299,22 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
     }
 }
 
+// Kernel arguments sit in memory that the runtime may place on the host side of the bus
+// (on some systems it does: every kernel then starts with a bus round trip). The compiler
+// loads each argument where it is first needed and reloads it when it runs short of
+// scalar registers, so a kernel can pay several such round trips, some of them late (in
+// its epilogue). An opaque copy of every 32-bit word at kernel entry issues all the
+// loads together and keeps the values in scalar registers from then on.
+template <typename T>
+__device__ __forceinline__ void pin_args(T& v) {
+    static_assert(sizeof(T) % 4 == 0, "32-bit words");
+    unsigned w[sizeof(T) / 4];
+    __builtin_memcpy(w, &v, sizeof(T));
+#pragma unroll
+    for (unsigned i = 0; i < sizeof(T) / 4; ++i) asm volatile("" : "+s"(w[i]));
+    __builtin_memcpy(&v, w, sizeof(T));
+}
+
 // Calls f(integral_constant<int, 0>) .. f(integral_constant<int, N-1>) in order: an
 // unrolled loop whose index is a compile-time constant in the body.
 template <int N, typename F>
