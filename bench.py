@@ -518,15 +518,30 @@ def main():
         def bwd_rope():
             cg.attn_bwd_dq(q, k, v, o, do, lse, scale=w.scale, delta=delta, dq=dq, stream=stream, rope=(rc, rs))
             cg.attn_bwd_dkv(q, k, v, do, lse, delta, scale=w.scale, dk=dk, dv=dv, stream=stream, rope=(rc, rs))
+        # The forward with Q and K turned as they are loaded (d = 64), against the pass
+        # followed by the plain forward.
+        fused = w.d == 64
+        o_f, lse_f = torch.empty_like(o), torch.empty_like(lse)
+        def fwd_rope():
+            cg.attn_fwd(q, k, v, scale=w.scale, o=o_f, lse=lse_f, rope=(rc, rs))
+        def pass_then_fwd():
+            rope_pass()
+            cg.attn_fwd(q_rot, k_rot, v, scale=w.scale, o=o_f, lse=lse_f)
         rope_pass(); bwd_rope()
+        if fused:
+            fwd_rope(); pass_then_fwd()
         torch.cuda.synchronize()
         ms_rope, ms_bwd_rope = graph_timed(rope_pass, args.steps), timed(bwd_rope, args.steps)
+        fused_ms = {}
+        if fused:
+            fused_ms = {"fused_fwd_ms": round(graph_timed(fwd_rope, args.steps), 5),
+                        "pass_then_fwd_ms": round(graph_timed(pass_then_fwd, args.steps), 5)}
         rope_bytes = 2 * 2 * w.B * w.T * (w.Hq + w.Hkv) * w.d + 2 * 4 * w.T * (w.d // 2)
         gbs = rope_bytes / (ms_rope * 1e-3) / 1e9
         out["rope"] = {"pass_ms": round(ms_rope, 5), "bytes": rope_bytes,
                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)},
-                       "bwd_ms": round(ms_bwd_rope, 5), "bwd_plain_ms": round(bwd_ms, 5)}
+                       "bwd_ms": round(ms_bwd_rope, 5), "bwd_plain_ms": round(bwd_ms, 5), **fused_ms}
     # The measured matrix-core peak (calibration kernel, the way the pages measure theirs):
     # one wave of workgroups (2 per CU, 8 waves per CU), every wave 4 independent chains of
     # 32x32x16 bf16 products on registers; HIP events around one launch; the kernel's own

@@ -64,6 +64,8 @@ def library():
         lib.cgqa_gemm.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, ctypes.c_size_t, vp]
         lib.attn_rope_qk.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp]
         lib.attn_rope_qk.restype = i
+        lib.attn_fwd_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.attn_fwd_rope.restype = i
         lib.attn_bwd_dq_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.attn_bwd_dq_rope.restype = i
         lib.attn_bwd_dkv_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
@@ -153,9 +155,11 @@ def _kv_stride(rk, rv):
     return rk
 
 
-def attn_fwd(q, k, v, scale=None, o=None, lse=None, stream=None):
+def attn_fwd(q, k, v, scale=None, o=None, lse=None, stream=None, rope=None):
     """o [B,T,Hq,d] bf16 and lse [B,Hq,T] fp32 for bf16 q [B,T,Hq,d], k, v [B,T,Hkv,d].
-    q, k, v and o may be row-strided views (e.g. of one packed QKV buffer)."""
+    q, k, v and o may be row-strided views (e.g. of one packed QKV buffer). With
+    rope=(cos, sin) (fp32 [T, d/2]), q and k are the unrotated, contiguous tensors and are
+    rotated as they are loaded (attn_fwd_rope, d = 64)."""
     torch = _torch()
     B, T, Hq, Hkv, d = _dims(q, k)
     rq = _need(q, "q", torch.bfloat16, (B, T, Hq, d), rows=True)
@@ -168,7 +172,14 @@ def attn_fwd(q, k, v, scale=None, o=None, lse=None, stream=None):
     ro = _need(o, "o", torch.bfloat16, (B, T, Hq, d), rows=True)
     _need(lse, "lse", torch.float32, (B, Hq, T))
     lib = library()
-    if (rq, rkv, ro) == (Hq * d, Hkv * d, Hq * d):
+    if rope is not None:
+        if (rq, rkv, ro) != (Hq * d, Hkv * d, Hq * d):
+            raise ValueError("attn_fwd with rope takes contiguous q, k, v and o")
+        cos, sin = _rope_tables(rope, T, d)
+        _check("attn_fwd_rope", lib.attn_fwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cos),
+                                                  _ptr(sin), B, T, Hq, Hkv, d, _scale(scale, d),
+                                                  _stream_ptr(stream)))
+    elif (rq, rkv, ro) == (Hq * d, Hkv * d, Hq * d):
         _check("attn_fwd", lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                         B, T, Hq, Hkv, d, _scale(scale, d), _stream_ptr(stream)))
     else:

@@ -68,10 +68,12 @@ int finish(hipError_t e) {
 }
 
 int fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
-             int B, int T, int Hq, int Hkv, int d, int q_rs, int kv_rs, int o_rs, float scale, void* stream) {
+             int B, int T, int Hq, int Hkv, int d, int q_rs, int kv_rs, int o_rs, float scale, void* stream,
+             bool rope = false, const float* rope_cos = nullptr, const float* rope_sin = nullptr) {
     bool empty = false;
     int rc = check_shape(B, T, Hq, Hkv, d, scale, &empty);
     if (rc != CGQA_OK) return rc;
+    if (rope && d != 64) return CGQA_EUNSUPPORTED;
     const int64_t rows = (int64_t)B * T, wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d;
     const int64_t rcs[3] = {check_stride(q_rs, wq, rows, 8), check_stride(kv_rs, wkv, rows, 8),
                             check_stride(o_rs, wq, rows, 4)};
@@ -88,6 +90,13 @@ int fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* 
     if (!disjoint(vo, vl)) return CGQA_EINVAL;
     for (const View& s : ins)
         if (!disjoint(s, vo) || !disjoint(s, vl)) return CGQA_EINVAL;
+    if (rope) {
+        if (!rope_cos || !rope_sin) return CGQA_EINVAL;
+        if (!aligned16(rope_cos) || !aligned16(rope_sin)) return CGQA_EUNSUPPORTED;
+        const int64_t nt = (int64_t)T * (d / 2);
+        const View vc{rope_cos, 1, nt, nt, 4}, vs{rope_sin, 1, nt, nt, 4};
+        if (!disjoint(vc, vo) || !disjoint(vc, vl) || !disjoint(vs, vo) || !disjoint(vs, vl)) return CGQA_EINVAL;
+    }
 
     cgqa::FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
@@ -95,6 +104,11 @@ int fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* 
     a.q_rs = q_rs; a.kv_rs = kv_rs; a.o_rs = o_rs;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
     a.div = cgqa::make_map_divs(B, Hq, Hkv);
+    if (rope) {
+        a.rope_cos = rope_cos;
+        a.rope_sin = rope_sin;
+        return finish(cgqa::launch_fwd_rope(a, (hipStream_t)stream));
+    }
     return finish(cgqa::launch_fwd(a, (hipStream_t)stream));
 }
 
@@ -402,6 +416,15 @@ int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* 
     const int64_t wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d;
     if (Hq < 1 || Hkv < 1 || wq >= ((int64_t)1 << 31)) return CGQA_EINVAL;
     return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, d, (int)wq, (int)wkv, (int)wq, scale, stream);
+}
+
+int attn_fwd_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                  const float* rope_cos, const float* rope_sin, int B, int T, int Hq, int Hkv, int d,
+                  float scale, void* stream) {
+    const int64_t wq = (int64_t)Hq * d, wkv = (int64_t)Hkv * d;
+    if (Hq < 1 || Hkv < 1 || wq >= ((int64_t)1 << 31)) return CGQA_EINVAL;
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, d, (int)wq, (int)wkv, (int)wq, scale, stream,
+                    true, rope_cos, rope_sin);
 }
 
 int attn_fwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,

@@ -47,7 +47,7 @@
 
 namespace cgqa {
 
-template <int D>
+template <int D, bool ROPE = false>
 struct FwdCfg {
     // Query blocks of 32 per wave (the code also supports two, which halves the LDS
     // fragment reads per product but needs ~236 registers and so at most two waves per
@@ -61,10 +61,11 @@ struct FwdCfg {
     // Keys per LDS tile: 64 at d = 64 (two 32-key blocks per barrier and per DMA batch,
     // three stages: 48 KB, three workgroups per CU; measured 0.3-8% faster than 32-key
     // tiles in five stages, except 2% slower at T = 4096), 32 at d = 128 (five stages:
-    // 80 KB, two workgroups per CU).
-    static constexpr int kBN = D == 64 ? 64 : 32;
+    // 80 KB, two workgroups per CU). With the rotary embedding (ROPE, d = 64 only) the
+    // tiles are 32 keys in five stages, 48 KB with the rotary tables.
+    static constexpr int kBN = (D == 64 && !ROPE) ? 64 : 32;
     static constexpr int kBPT = kBN / 32;                   // 32-key blocks per tile
-    static constexpr int kStages = D == 64 ? 3 : 5;
+    static constexpr int kStages = (D == 64 && !ROPE) ? 3 : 5;
     // Tiles issued beyond the one a barrier waits for. At the barrier for tile t the
     // stage of tile t - 2 (kBPT = 2) or t - 3 (kBPT = 1) has been read for the last
     // time, which leaves kStages - 2 resp. kStages - 3 stages for tiles in flight.
@@ -74,23 +75,30 @@ struct FwdCfg {
     static constexpr int kRow = D * 2;                      // bytes per K or V row in LDS
     static constexpr int kTile = kBN * kRow;                // bytes per K (or V) tile
     static constexpr int kStage = 2 * kTile;                // K then V
-    static constexpr int kLds = kStages * kStage;
+    static constexpr int kRing = kStages * kStage;
     static constexpr int kLoadsPerTensor = kTile / 1024 / kWaves;   // 1 KB per wave instruction
     static constexpr int kLoadsPerTile = 2 * kLoadsPerTensor;       // per wave
     static constexpr int kRowsPerLoad = 1024 / kRow;
     static constexpr int kUnroll = kStages * kBPT;          // period of the block -> stage map
+    // ROPE: each thread's cosines and sines for the K chunks it loads (16 bytes of each
+    // per chunk), by DMA into an area of its own after the ring.
+    static constexpr int kTabHalf = ROPE ? kLoadsPerTensor * kWaves * 1024 : 0;
+    static constexpr int kLds = kRing + 2 * kTabHalf;
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(kTile % (1024 * kWaves) == 0, "tile load must split evenly over the waves");
     static_assert(kAhead * kBN >= 64, "prefetch distance: at least 64 keys in flight");
+    // The rotary path turns each 32-key tile once (one block per tile) and exists at
+    // d = 64 only: at d = 128 its extra registers would spill.
+    static_assert(!ROPE || (kBPT == 1 && D == 64), "rotary configuration");
     static_assert(2 * kLds <= 160 * 1024, "two workgroups per CU");
 };
 
 // Probabilities above this trigger a move of the reference max.
 constexpr float kRescaleLimit = 1099511627776.0f;   // 2^40
 
-template <int D>
+template <int D, bool ROPE>
 __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(FwdArgs a) {
-    using C = FwdCfg<D>;
+    using C = FwdCfg<D, ROPE>;
     constexpr int NQB = C::kNQB;
     constexpr int kAll = (1 << NQB) - 1;   // bit qb: query block qb of the wave
     __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
@@ -178,6 +186,55 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(FwdArgs 
             }
         }
     };
+    // ROPE: the rotary tables of the K chunks this thread loads (pairs 4c .. 4c+3 of its
+    // chunk c, row clamped like the chunk's), by DMA into the thread's own 16 bytes of the
+    // cosine and sine areas; after this thread's loads of a tile have landed it turns its
+    // own chunks in place (no other thread's data is involved, so only the barrier that
+    // publishes the tile follows).
+    char* const tab = smem + C::kRing;
+    unsigned tab_off[C::kLoadsPerTensor];
+#pragma unroll
+    for (int i = 0; i < C::kLoadsPerTensor; ++i)
+        tab_off[i] = (unsigned)(ld_row[i] * (D / 2) + 4 * (int)(ld_chunk_b[i] / 16)) * 4u;
+    auto issue_tables = [&](int jt) CGQA_INLINE {
+        const int row0 = jt * C::kBN;
+#pragma unroll
+        for (int i = 0; i < C::kLoadsPerTensor; ++i) {
+            char* dst = tab + (wave * C::kLoadsPerTensor + i) * 1024;
+            if (row0 + C::kBN <= T) {
+                load_lds16_off(a.rope_cos + (size_t)row0 * (D / 2), tab_off[i], dst);
+                load_lds16_off(a.rope_sin + (size_t)row0 * (D / 2), tab_off[i], dst + C::kTabHalf);
+            } else {
+                const unsigned off = (unsigned)(min(row0 + ld_row[i], T - 1) * (D / 2) + 4 * (int)(ld_chunk_b[i] / 16)) * 4u;
+                load_lds16_off(a.rope_cos, off, dst);
+                load_lds16_off(a.rope_sin, off, dst + C::kTabHalf);
+            }
+        }
+    };
+    auto turn_tile = [&](int jt) CGQA_INLINE {
+        char* ks = smem + (jt % C::kStages) * C::kStage;
+#pragma unroll
+        for (int i = 0; i < C::kLoadsPerTensor; ++i) {
+            const int o = (wave * C::kLoadsPerTensor + i) * 1024 + 16 * lane;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(ks + o);
+            const f32x4 cs = *reinterpret_cast<const f32x4*>(tab + o);
+            const f32x4 sn = *reinterpret_cast<const f32x4*>(tab + C::kTabHalf + o);
+            *reinterpret_cast<u32x4*>(ks + o) = rope_turn8(x, cs, sn);
+        }
+    };
+    // ROPE, tile t: its loads and its tables were issued before the newest load in
+    // flight (tile t + kAhead - 1, issued after the tables of tile t), so waiting for
+    // all but that one completes them; turn it, publish it, then load the next tables
+    // (this thread's reads of the area are done) and the tile kAhead ahead.
+    auto turn_and_advance = [&](int t) CGQA_INLINE {
+        static_assert(!ROPE || C::kAhead >= 2, "the wait below assumes a later tile in flight");
+        if (t + C::kAhead - 1 < ntiles) wait_vm<C::kLoadsPerTile>();
+        else wait_vm<0>();
+        turn_tile(t);
+        lds_barrier();
+        if (t + 1 < ntiles) issue_tables(t + 1);
+        if (t + C::kAhead < ntiles) issue_tile(t + C::kAhead);
+    };
     // Waits until tile t is in LDS for every wave. Tiles t+1 .. min(t+ahead, ntiles-1)
     // may still be in flight (issued after t, so counted after it).
     auto wait_tile = [&](int t, int ahead) CGQA_INLINE {
@@ -193,13 +250,28 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(FwdArgs 
         if ((j + 1) % C::kBPT != 0) return;
         const int t = (j + 1) / C::kBPT;
         if (t >= ntiles) return;
-        wait_tile(t, C::kAhead - 1);
-        if (t + C::kAhead < ntiles) issue_tile(t + C::kAhead);
+        if constexpr (ROPE) {
+            turn_and_advance(t);
+        } else {
+            wait_tile(t, C::kAhead - 1);
+            if (t + C::kAhead < ntiles) issue_tile(t + C::kAhead);
+        }
     };
 
+    if constexpr (ROPE) {
+        // Tables and tile 0, then tiles 1 .. kAhead-1; the first turn issues the rest.
+        if (ntiles > 0) {
+            issue_tables(0);
+            issue_tile(0);
+        }
 #pragma unroll
-    for (int t = 0; t <= C::kAhead; ++t)
-        if (t < ntiles) issue_tile(t);
+        for (int t = 1; t < C::kAhead; ++t)
+            if (t < ntiles) issue_tile(t);
+    } else {
+#pragma unroll
+        for (int t = 0; t <= C::kAhead; ++t)
+            if (t < ntiles) issue_tile(t);
+    }
 
     // Q as the B operand: lane (query n of block qb, group hl) holds dims
     // 16*kd + 8*hl .. +7.
@@ -210,7 +282,14 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(FwdArgs 
 #pragma unroll
         for (int kd = 0; kd < C::kKD; ++kd) {
             u32x4 x = {0u, 0u, 0u, 0u};
-            if (row < T) x = load16(qbase + (size_t)row * q_stride + 16 * kd + 8 * hl);
+            if (row < T) {
+                x = load16(qbase + (size_t)row * q_stride + 16 * kd + 8 * hl);
+                if constexpr (ROPE) {
+                    const size_t ti = (size_t)row * (D / 2) + 8 * kd + 4 * hl;
+                    x = rope_turn8(x, *reinterpret_cast<const f32x4*>(a.rope_cos + ti),
+                                   *reinterpret_cast<const f32x4*>(a.rope_sin + ti));
+                }
+            }
             qreg[qb][kd] = __builtin_bit_cast(bf16x8, x);
         }
     }
@@ -386,7 +465,11 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(FwdArgs 
 
         // the matrix core beside the softmax of block j.
         // ---- prologue: tile 0, scores of block 0 and the reference maximum.
-        wait_tile(0, C::kAhead);
+        if constexpr (ROPE) {
+            if (ntiles > 0) turn_and_advance(0);
+        } else {
+            wait_tile(0, C::kAhead);
+        }
         if (active) {
             scores(0, kAll, s_cur);
             f32x16 sm = s_cur[0];
@@ -447,15 +530,15 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(FwdArgs 
     }
 }
 
-template <int D>
+template <int D, bool ROPE>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-    using C = FwdCfg<D>;
+    using C = FwdCfg<D, ROPE>;
     FwdArgs x = a;
     x.n_qtiles = (a.T + C::kBM - 1) / C::kBM;
     x.n_pairs = a.B * a.Hkv;
     x.xcd_group = x.n_pairs % 8 == 0 ? 1 : 0;
     const long blocks = (long)x.n_qtiles * a.B * a.Hq;
-    hipLaunchKernelGGL((attn_fwd_kernel<D>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, x);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, ROPE>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, x);
     return hipGetLastError();
 }
 
@@ -463,8 +546,15 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 // key-split kernel (attn_fwd_par.hip), every other shape to the tiled kernel above.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     if (fwd_split_keys_chosen(a)) return launch_fwd_split_keys(a, stream);
-    if (a.d == 64) return launch_fwd_t<64>(a, stream);
-    return launch_fwd_t<128>(a, stream);
+    if (a.d == 64) return launch_fwd_t<64, false>(a, stream);
+    return launch_fwd_t<128, false>(a, stream);
+}
+
+// The rotary forward (d = 64) always runs the tiled kernel (the key-split one has no
+// rotary variant).
+hipError_t launch_fwd_rope(const FwdArgs& a, hipStream_t stream) {
+    if (a.d != 64) return hipErrorInvalidValue;
+    return launch_fwd_t<64, true>(a, stream);
 }
 
 }  // namespace cgqa

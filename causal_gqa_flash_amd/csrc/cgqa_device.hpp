@@ -335,11 +335,57 @@ __device__ __forceinline__ void wait_tiles_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Wait until at most N vector memory operations of this wave are outstanding (no
+// barrier, LDS operations not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for
 // its global loads and stores (which __syncthreads() would drain too), then joins the
 // barrier. Enough when the barrier only orders LDS writes before LDS reads.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Rotary embedding, forward: eight consecutive bf16 dims (four interleaved pairs, as
+// loaded) turned by the cosines c and sines s of their pairs, y0 = x0 c - x1 s and
+// y1 = x0 s + x1 c, each rounded to bf16 (nearest even) from the exact value.
+// A bf16 input times an fp32 table value has at most 32 significant bits, so it is exact
+// in fp64, and fma(x0, c, -(x1 s)) in fp64 rounds the exact y a single time, to 53 bits.
+// Rounding that to fp32 and then to bf16 can only go wrong where the fp32 value lands
+// exactly on a bf16 tie (low 16 bits 0x8000); there the fp64 value says on which side of
+// the tie y lies, and the fp32 value is moved one unit that way before its rounding to
+// bf16. The one case left is an exact y within 2^-53 of a tie without being one (bits 10
+// to 53 of its significand all equal), which fp64 cannot resolve.
+__device__ __forceinline__ float rope_bf16_ready(double y) {
+    const float f = (float)y;
+    unsigned u = __float_as_uint(f);
+    if ((u & 0xFFFFu) == 0x8000u) {
+        const double fd = (double)f;
+        if (y != fd) u = ((y > fd) == (f > 0.0f)) ? u + 1u : u - 1u;
+    }
+    return __uint_as_float(u);
+}
+__device__ __forceinline__ u32x4 rope_turn8(u32x4 raw, f32x4 c, f32x4 s) {
+    const bf16x8 x = __builtin_bit_cast(bf16x8, raw);
+    f32x4 lo, hi;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const double x0 = (double)(float)x[2 * p], x1 = (double)(float)x[2 * p + 1];
+        const double cp = (double)c[p], sp = (double)s[p];
+        const double y0 = fma(x0, cp, -(x1 * sp));
+        const double y1 = fma(x0, sp, x1 * cp);
+        if (p < 2) { lo[2 * p] = rope_bf16_ready(y0); lo[2 * p + 1] = rope_bf16_ready(y1); }
+        else { hi[2 * p - 4] = rope_bf16_ready(y0); hi[2 * p - 3] = rope_bf16_ready(y1); }
+    }
+    const u32x2 wlo = __builtin_bit_cast(u32x2, __builtin_convertvector(lo, bf16x4));
+    const u32x2 whi = __builtin_bit_cast(u32x2, __builtin_convertvector(hi, bf16x4));
+    u32x4 y;
+    y[0] = wlo[0]; y[1] = wlo[1]; y[2] = whi[0]; y[3] = whi[1];
+    return y;
 }
 
 // Rotary embedding, backward. The cosines and sines of the two pairs that start at dim

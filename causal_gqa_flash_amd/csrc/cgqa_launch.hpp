@@ -51,6 +51,8 @@ struct FwdArgs {
     int n_qtiles;       // set by the launcher: query tiles per (batch, head)
     int n_pairs;        // set by the launcher: B * Hkv (batch, kv head) slices
     int xcd_group;      // set by the launcher: keep each slice's tiles on one XCD
+    const float* rope_cos;   // rotary tables [T][d/2] when the kernel turns Q and K itself
+    const float* rope_sin;   // (attn_fwd_rope); unused otherwise
     MapDivs div;        // set by the C-ABI layer
 };
 
@@ -141,6 +143,8 @@ struct RopeArgs {
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// The forward with the rotary embedding applied to Q and K as they are loaded.
+hipError_t launch_fwd_rope(const FwdArgs& a, hipStream_t stream);
 // Forward with every query block's keys split over two waves (attn_fwd_par.hip), for
 // d = 64 grids that would not fill the chip with the tiled kernel.
 bool fwd_split_keys_chosen(const FwdArgs& a);

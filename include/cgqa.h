@@ -165,6 +165,17 @@ int attn_bwd_dkv_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v
  * any other overlap of an output is CGQA_EINVAL. The forward then runs attn_fwd on the
  * rotated tensors.
  *
+ * attn_fwd_rope is attn_fwd on q and k rotated as they are loaded, with no rotated copy
+ * written: q and k are the unrotated contiguous tensors, and o and lse are those of
+ * attention on the rotated ones, each rotated value rounded exactly as attn_rope_qk
+ * rounds it (the same bits as attn_rope_qk followed by attn_fwd wherever attn_fwd runs
+ * its tiled kernel, i.e. at least three 128-query workgroups per CU). d = 64 only
+ * (CGQA_EUNSUPPORTED otherwise); missing tables are CGQA_EINVAL, tables not 16-byte
+ * aligned CGQA_EUNSUPPORTED, tables overlapping o or lse CGQA_EINVAL. Every workgroup
+ * that reads a K tile turns it again, so this call is slower than attn_rope_qk followed
+ * by attn_fwd; it serves callers that keep no rotated copy of q and k. A backward on its
+ * outputs needs the rotated tensors (attn_rope_qk) all the same.
+ *
  * attn_bwd_dq_rope / attn_bwd_dkv_rope are attn_bwd_dq / attn_bwd_dkv on the rotated q and k
  * (contiguous, fp32 gradients) whose dq and dk are turned back inside the kernels, before
  * they are stored, to the gradients with respect to the unrotated q and k:
@@ -174,6 +185,10 @@ int attn_rope_qk(const uint16_t* q, const uint16_t* k, uint16_t* q_out, uint16_t
                  const float* cos, const float* sin, int B, int T, int Hq, int Hkv, int d,
                  int q_row_stride, int k_row_stride, int q_out_row_stride, int k_out_row_stride,
                  void* stream);
+
+int attn_fwd_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                  const float* cos, const float* sin, int B, int T, int Hq, int Hkv, int d,
+                  float scale, void* stream);
 
 int attn_bwd_dq_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      const uint16_t* o, const uint16_t* dO, const float* lse,

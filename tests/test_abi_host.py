@@ -429,6 +429,31 @@ def test_rope_backward_rejections():
         assert fn(*q, *args) == cg.CGQA_EINVAL
 
 
+def test_rope_forward_rejections():
+    """attn_fwd_rope: q k v o lse cos sin; the forward's own checks, then the tables'."""
+    lib = cg.library()
+    p = [fake(j) for j in range(7)]
+
+    def call(ptrs, B=1, T=64, Hq=6, Hkv=2, d=64):
+        return lib.attn_fwd_rope(*ptrs, B, T, Hq, Hkv, d, 0.125, None)
+
+    for i in range(7):
+        q = list(p)
+        q[i] = None
+        assert call(q) == cg.CGQA_EINVAL, i
+        q = list(p)
+        q[i] += 8
+        assert call(q) == cg.CGQA_EUNSUPPORTED, i
+    assert call(p, d=128) == cg.CGQA_EUNSUPPORTED          # d = 64 only
+    assert call(p, Hq=6, Hkv=4) == cg.CGQA_EINVAL
+    for t in (5, 6):                                        # a table inside an output
+        for out in (3, 4):
+            q = list(p)
+            q[t] = q[out] + 64
+            assert call(q) == cg.CGQA_EINVAL, (t, out)
+    assert call([None] * 7, T=0) == cg.CGQA_OK
+
+
 def test_gemm_static_rejects_shapes_beyond_its_scratch():
     """cgqa_gemm_static keeps split-K partials in a fixed device array: a shape whose
     split needs more is CGQA_EINVAL before any HIP call; the usual rules still apply."""

@@ -111,3 +111,68 @@ def test_rotary_pipeline_matches_oracle(B, T, Hq, Hkv, d, seed):
     want["dk"] = orope.rotate_back(want["dk"], c, s)
     ok, msg = check_all(got, want)
     assert ok, msg
+
+
+FUSED_SHAPES = [s for s in SHAPES if s[4] == 64] + [(16, 500, 12, 4, 64, 56)]
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,d,seed", FUSED_SHAPES)
+def test_fused_rotary_forward_matches_oracle(B, T, Hq, Hkv, d, seed):
+    """attn_fwd_rope (q and k turned as they are loaded) against the fp64 oracle of the
+    exactly rotated inputs, at the attention tolerances."""
+    import torch
+    print(f"fused rope forward B={B} T={T} Hq={Hq} Hkv={Hkv} d={d}", flush=True)
+    x = si.make_inputs(B, T, Hq, Hkv, d, seed, 1.0)
+    c, s, dc, ds = _tables(T, d)
+    scale = workload_scale(d)
+    dev = to_device(x)
+    o, lse = cg.attn_fwd(dev["q"], dev["k"], dev["v"], scale=scale, rope=(dc, ds))
+    torch.cuda.synchronize()
+    xr = dict(x)
+    xr["q"] = si.f32_to_bf16_bits(orope.rotate_bf16(x["q"], c, s).astype(np.float32))
+    xr["k"] = si.f32_to_bf16_bits(orope.rotate_bf16(x["k"], c, s).astype(np.float32))
+    want = oracle_run(xr, scale, backward=False)
+    ok, msg = check_all(dict(o=_np(o), lse=_np(lse)), want, keys=("o", "lse"))
+    assert ok, msg
+
+
+def test_fused_rotary_forward_bits_on_a_quarter_turn():
+    """With cos = 0 and sin = 1 the turn (x0, x1) -> (-x1, x0) is exact in bf16, so the
+    fused forward must give the plain forward's bits on inputs turned on the host (a grid
+    where the plain forward also runs the tiled kernel; T = 500 leaves a ragged tile whose
+    table rows are clamped)."""
+    import torch
+    B, T, Hq, Hkv, d = 16, 500, 12, 4, 64
+    x = si.make_inputs(B, T, Hq, Hkv, d, 57, 1.0)
+    dev = to_device(x)
+    cos = torch.zeros((T, d // 2), dtype=torch.float32, device="cuda")
+    sin = torch.ones((T, d // 2), dtype=torch.float32, device="cuda")
+
+    def quarter(t):
+        y = torch.empty_like(t)
+        y[..., 0::2] = -t[..., 1::2]
+        y[..., 1::2] = t[..., 0::2]
+        return y
+
+    o, lse = cg.attn_fwd(dev["q"], dev["k"], dev["v"], scale=0.125, rope=(cos, sin))
+    o2, lse2 = cg.attn_fwd(quarter(dev["q"]), quarter(dev["k"]), dev["v"], scale=0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+
+
+def test_fused_rotary_forward_bits_equal_pass_plus_forward():
+    """The fused forward rounds every rotated value as the rotation pass does, so at the
+    bench workload (where the plain forward runs the tiled kernel) it gives the bits of
+    the pass followed by the plain forward."""
+    import torch
+    B, T, Hq, Hkv, d = 16, 1024, 6, 2, 64
+    x = si.make_inputs(B, T, Hq, Hkv, d, 3, 1.0)
+    _, _, dc, ds = _tables(T, d)
+    dev = to_device(x)
+    o, lse = cg.attn_fwd(dev["q"], dev["k"], dev["v"], scale=0.125, rope=(dc, ds))
+    qr, kr = cg.rope_qk(dev["q"], dev["k"], dc, ds)
+    o2, lse2 = cg.attn_fwd(qr, kr, dev["v"], scale=0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse, lse2)
