@@ -47,6 +47,13 @@ SMALL = [
     # shapes just past that size run the four-block dealing with its zig-zag order
     (17, 100, 6, 2, 64, 22, 1.0),
     (12, 300, 3, 1, 64, 23, 2.0),
+    # more heads per dK/dV slot: G = 4 and G = 12 (four slots of one and of three heads),
+    # G = 16 (four heads per slot), G = 5 (one slot of five heads); d = 128 with T = 1
+    (2, 190, 8, 2, 64, 24, 1.0),
+    (1, 70, 12, 1, 64, 25, 1.0),
+    (1, 100, 16, 1, 64, 26, 2.0),
+    (2, 90, 5, 1, 64, 27, 1.0),
+    (1, 1, 4, 2, 128, 28, 1.0),
 ]
 
 
