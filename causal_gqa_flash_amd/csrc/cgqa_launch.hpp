@@ -8,6 +8,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <numeric>
+#include <vector>
+
 namespace cgqa {
 
 // Floor division by a divisor fixed at launch, on the scalar unit. For 0 <= n < 2^31 and
@@ -54,6 +58,11 @@ struct FwdArgs {
     const float* rope_cos;   // rotary tables [T][d/2] when the kernel turns Q and K itself
     const float* rope_sin;   // (attn_fwd_rope); unused otherwise
     MapDivs div;        // set by the C-ABI layer
+    // Set by the launcher: when perm_n > 0, workgroup x of XCD x % 8 takes the tile at
+    // position perm[x >> 3] of the heaviest-first order instead of position x >> 3 (see
+    // balance_one_round).
+    int perm_n;
+    unsigned char perm[256];
 };
 
 struct BwdArgs {
@@ -154,5 +163,52 @@ hipError_t launch_bwd_dkv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_naive_fwd(const NaiveArgs& a, hipStream_t stream);
 hipError_t launch_naive_bwd(const NaiveArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+
+// Dispatch order of a grid that fits the chip in one residency round (every workgroup
+// resident from the start). On gfx950 the workgroups of one XCD go to its C CUs in launch
+// order, one per CU per pass: the workgroups with local index i, C + i, 2C + i, ... of an
+// XCD share one CU (measured: a probe that recorded the hardware ids of every wave of such
+// a launch). With tiles launched heaviest first, the CU that receives the heaviest tile of
+// the first pass also receives the heaviest of every later pass, and the kernel lasts as
+// long as that CU's sum. Here the passes are filled greedily instead: pass by pass, the
+// heaviest remaining tiles go to the CUs with the least work so far. weight(p), p in
+// [0, L), is the work of position p of the heaviest-first order and must not increase with
+// p. Writes perm[local] = position and returns L, or returns 0 (keep the heaviest-first
+// order) when the grid is larger than one round or than the table. Any permutation gives
+// the same results; only the balance changes.
+// CUs per XCD of the current device (gfx950: eight XCDs).
+inline int cus_per_xcd() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return n / 8;
+}
+
+template <typename W>
+inline int balance_one_round(unsigned char* perm, int L, int C, int S, W weight) {
+    if (L <= 0 || C <= 0 || L > C * S || L > 256) return 0;
+    const int passes = (L + C - 1) / C;
+    std::vector<long> load(C, 0);
+    std::vector<int> cu_of(L), order(C);
+    for (int r = 0; r < passes; ++r) {
+        std::iota(order.begin(), order.end(), 0);
+        std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return load[a] < load[b]; });
+        const int p0 = r * C, n = std::min(C, L - p0);
+        for (int k = 0; k < n; ++k) {
+            cu_of[p0 + k] = order[k];
+            load[order[k]] += weight(p0 + k);
+        }
+    }
+    // The CUs that take a tile in a last, partial pass must be those that local indices
+    // r*C + 0 .. r*C + n-1 reach: relabel them 0 .. n-1 (the same labels in every pass).
+    std::vector<int> label(C, -1);
+    const int last0 = (passes - 1) * C, nlast = L - last0;
+    int next = 0;
+    for (int k = 0; k < nlast; ++k) label[cu_of[last0 + k]] = next++;
+    for (int c = 0; c < C; ++c)
+        if (label[c] < 0) label[c] = next++;
+    for (int p = 0; p < L; ++p) perm[(p / C) * C + label[cu_of[p]]] = (unsigned char)p;
+    return L;
+}
 
 }  // namespace cgqa
