@@ -416,29 +416,6 @@ def main():
         del graph
         return float(np.median(per))
 
-    def step_kernel_times(n, calls=None):
-        """Each kernel's mean launch duration inside the step loop: HIP events recorded on
-        the stream before the step and after each of its three calls, for n steps; an
-        event after a call completes when the call's kernel does, so consecutive events
-        bracket one kernel (for steps of 100 us and more the host dispatches a step in
-        about half the step's GPU time, so no kernel waits for its launch). Median over
-        repeats."""
-        names = ("attn_fwd", "attn_bwd_dq", "attn_bwd_dkv")
-        calls = calls or (fwd, bwd_dq, bwd_dkv)
-        per = {k: [] for k in names}
-        for _ in range(args.repeats):
-            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
-            torch.cuda.synchronize()
-            for i in range(n):
-                ev[i][0].record(stream)
-                for j, fn in enumerate(calls):
-                    fn()
-                    ev[i][j + 1].record(stream)
-            torch.cuda.synchronize()
-            for j, name in enumerate(names):
-                per[name].append(sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n)) / n)
-        return {k: float(np.median(v)) for k, v in per.items()}
-
     # Clock settle: untimed steps until settle_ms of wall time has passed, then the W
     # warmup steps. Both run the full step; neither is inside the timed region.
     settle_steps = 0
@@ -454,14 +431,12 @@ def main():
 
     # Whole-step timing: exactly `steps` steps between synchronisations.
     ms_step = timed(step, args.steps)
-    # Each kernel's average launch duration inside the step loop (events between the
-    # calls of every step). Beside it, a captured HIP graph of `steps` back-to-back
-    # launches of one kernel alone, replayed: the forward runs about 15% longer that way
-    # than inside the step (the kernel trace of both loops agrees), so the in-step figure
-    # is the one the step is made of. The graph-replayed step is timed as well.
-    ms_k = step_kernel_times(args.steps)
-    ms_b2b = {"attn_fwd": graph_timed(fwd, args.steps), "attn_bwd_dq": graph_timed(bwd_dq, args.steps),
-              "attn_bwd_dkv": graph_timed(bwd_dkv, args.steps)}
+    # Each kernel's average launch duration: a captured HIP graph of `steps` back-to-back
+    # launches of it, replayed (no host dispatch in the timed region; a short kernel timed
+    # in a Python loop is bounded by the host's dispatch of each call instead). The
+    # graph-replayed step is timed the same way.
+    ms_k = {"attn_fwd": graph_timed(fwd, args.steps), "attn_bwd_dq": graph_timed(bwd_dq, args.steps),
+            "attn_bwd_dkv": graph_timed(bwd_dkv, args.steps)}
     ms_step_graph = graph_timed(step, args.steps)
 
     pairs = w.causal_pairs
@@ -478,8 +453,7 @@ def main():
     for name in ms_k:
         a = fl[name] / (ms_k[name] * 1e-3) / 1e12
         kernels[name] = {"ms": round(ms_k[name], 5), "tflops": round(a, 2),
-                         "frac": round(a / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(name),
-                         "ms_back_to_back": round(ms_b2b[name], 5)}
+                         "frac": round(a / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(name)}
 
     out = {
         "metric": "causal attention TFLOP/s fwd and fwd+bwd, % of bf16 MFMA peak, 1xMI355X",
@@ -504,10 +478,9 @@ def main():
         "fwdbwd_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "compute": "fwd bf16 matrix core; bwd fp16 matrix core (dO and dS scaled by powers of two); "
                    "fp32 accumulation and softmax",
-        "kernel_timing": "kernels.ms: HIP events between the three calls of each of `steps` steps "
-                         "of the step loop; kernels.ms_back_to_back: a replayed HIP graph of `steps` "
-                         "back-to-back launches of the kernel alone; ms_per_step: the plain loop of "
-                         "`steps` steps; ms_per_step_graph: a replayed graph of `steps` steps",
+        "kernel_timing": "kernels: HIP events around a replayed HIP graph of `steps` back-to-back "
+                         "launches of each; ms_per_step: the plain loop of `steps` steps; "
+                         "ms_per_step_graph: a replayed graph of `steps` steps",
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -598,11 +571,9 @@ def main():
     del c_sink, c_clk
 
     if not args.no_configs:
-        # Every workload: the step from a replayed HIP graph of steps, each kernel as above
-        # (events inside the step loop) where a step takes 100 us or more, else from replays
-        # of a graph of the kernel's launches (the small workloads' kernels are shorter than
-        # their host dispatch); credited flops per causal pair as above, against the spec
-        # and the measured peak.
+        # Every workload: each kernel's share of a step as above, but from replays of captured
+        # HIP graphs (the small workloads' kernels are shorter than their host dispatch);
+        # credited flops per causal pair as above, against the spec and the measured peak.
         cfgs = {}
         for wi, wk in enumerate(si.WORKLOADS):
             xw = si.make_workload_inputs(wk, seed=wi + 1)
@@ -625,15 +596,9 @@ def main():
                 for fn in fns:
                     fn()
             torch.cuda.synchronize()
+            ms3 = [graph_timed(fn, n) for fn in fns]
             st_ms = graph_timed(lambda: [fn() for fn in fns], n)
-            if st_ms >= 0.1:
-                tk = step_kernel_times(n, fns)
-                ms3 = [tk["attn_fwd"], tk["attn_bwd_dq"], tk["attn_bwd_dkv"]]
-                how = "events in the step loop"
-            else:
-                ms3 = [graph_timed(fn, n) for fn in fns]
-                how = "graph of back-to-back launches"
-            entry = {"steps": n, "kernel_timing": how}
+            entry = {"steps": n}
             for name, ms_, per_pair in zip(("attn_fwd", "attn_bwd_dq", "attn_bwd_dkv"), ms3, (4, 6, 8)):
                 tf = per_pair * wk.d * wk.causal_pairs / (ms_ * 1e-3) / 1e12
                 entry[name] = {"ms": round(ms_, 5), "tflops": round(tf, 1),
