@@ -41,7 +41,7 @@
 //    then serves that slice's K and V to every query head of the group; on each XCD the
 //    heaviest query tiles (the most keys) are dispatched first, or, when every
 //    workgroup of the grid is resident from the start, in an order that gives each CU
-//    about the same number of key blocks (balance_one_round: 7% faster at B16 T1024).
+//    about the same number of key blocks (balance_one_round: 4.5% faster at B16 T1024).
 #include "cgqa_device.hpp"
 #include "cgqa_launch.hpp"
 

@@ -9,8 +9,6 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <numeric>
-#include <vector>
 
 namespace cgqa {
 
@@ -164,6 +162,14 @@ hipError_t launch_naive_fwd(const NaiveArgs& a, hipStream_t stream);
 hipError_t launch_naive_bwd(const NaiveArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 
+// CUs per XCD of the current device (gfx950: eight XCDs); 0 if the runtime cannot say.
+inline int cus_per_xcd() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return n / 8;
+}
+
 // Dispatch order of a grid that fits the chip in one residency round (every workgroup
 // resident from the start). On gfx950 the workgroups of one XCD go to its C CUs in launch
 // order, one per CU per pass: the workgroups with local index i, C + i, 2C + i, ... of an
@@ -175,24 +181,17 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 // [0, L), is the work of position p of the heaviest-first order and must not increase with
 // p. Writes perm[local] = position and returns L, or returns 0 (keep the heaviest-first
 // order) when the grid is larger than one round or than the table. Any permutation gives
-// the same results; only the balance changes.
-// CUs per XCD of the current device (gfx950: eight XCDs).
-inline int cus_per_xcd() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 0;
-    return n / 8;
-}
-
+// the same results; only the balance changes. No allocation: fixed arrays on the stack.
 template <typename W>
 inline int balance_one_round(unsigned char* perm, int L, int C, int S, W weight) {
-    if (L <= 0 || C <= 0 || L > C * S || L > 256) return 0;
+    constexpr int kMax = 256;
+    if (L <= 0 || C <= 0 || C > kMax || L > C * S || L > kMax) return 0;
     const int passes = (L + C - 1) / C;
-    std::vector<long> load(C, 0);
-    std::vector<int> cu_of(L), order(C);
+    long load[kMax] = {};
+    int cu_of[kMax], order[kMax], label[kMax];
     for (int r = 0; r < passes; ++r) {
-        std::iota(order.begin(), order.end(), 0);
-        std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return load[a] < load[b]; });
+        for (int c = 0; c < C; ++c) order[c] = c;
+        std::stable_sort(order, order + C, [&](int a, int b) { return load[a] < load[b]; });
         const int p0 = r * C, n = std::min(C, L - p0);
         for (int k = 0; k < n; ++k) {
             cu_of[p0 + k] = order[k];
@@ -201,7 +200,7 @@ inline int balance_one_round(unsigned char* perm, int L, int C, int S, W weight)
     }
     // The CUs that take a tile in a last, partial pass must be those that local indices
     // r*C + 0 .. r*C + n-1 reach: relabel them 0 .. n-1 (the same labels in every pass).
-    std::vector<int> label(C, -1);
+    for (int c = 0; c < C; ++c) label[c] = -1;
     const int last0 = (passes - 1) * C, nlast = L - last0;
     int next = 0;
     for (int k = 0; k < nlast; ++k) label[cu_of[last0 + k]] = next++;

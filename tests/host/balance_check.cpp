@@ -4,7 +4,9 @@
 // share CU i) must carry no more than under the heaviest-first order.
 #include "../../causal_gqa_flash_amd/csrc/cgqa_launch.hpp"
 
+#include <algorithm>
 #include <cstdio>
+#include <vector>
 
 int main() {
     int failures = 0, checked = 0;
