@@ -438,6 +438,14 @@ def main():
     ms_k = {"attn_fwd": graph_timed(fwd, args.steps), "attn_bwd_dq": graph_timed(bwd_dq, args.steps),
             "attn_bwd_dkv": graph_timed(bwd_dkv, args.steps)}
     ms_step_graph = graph_timed(step, args.steps)
+    # Each kernel's share of the step as the step runs it: a replayed graph of `steps`
+    # steps less a replayed graph of `steps` steps without that kernel (the others keep
+    # their order). A kernel alone back to back runs differently from the step (the
+    # forward about 15% longer); events between the calls would add their own time.
+    pair_ms = {"attn_fwd": graph_timed(lambda: (bwd_dq(), bwd_dkv()), args.steps),
+               "attn_bwd_dq": graph_timed(lambda: (fwd(), bwd_dkv()), args.steps),
+               "attn_bwd_dkv": graph_timed(lambda: (fwd(), bwd_dq()), args.steps)}
+    ms_in_step = {k: ms_step_graph - v for k, v in pair_ms.items()}
 
     pairs = w.causal_pairs
     fl = {"attn_fwd": 4 * w.d * pairs, "attn_bwd_dq": 6 * w.d * pairs, "attn_bwd_dkv": 8 * w.d * pairs}
@@ -452,8 +460,11 @@ def main():
     kernels = {}
     for name in ms_k:
         a = fl[name] / (ms_k[name] * 1e-3) / 1e12
+        a_in = fl[name] / (ms_in_step[name] * 1e-3) / 1e12 if ms_in_step[name] > 0 else None
         kernels[name] = {"ms": round(ms_k[name], 5), "tflops": round(a, 2),
-                         "frac": round(a / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(name)}
+                         "frac": round(a / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(name),
+                         "ms_in_step": round(ms_in_step[name], 5),
+                         "frac_in_step": round(a_in / PEAK_BF16_TFLOPS, 4) if a_in else None}
 
     out = {
         "metric": "causal attention TFLOP/s fwd and fwd+bwd, % of bf16 MFMA peak, 1xMI355X",
@@ -474,13 +485,16 @@ def main():
                    "pass": "fwd+bwd", "inputs": "bf16 N(0,1), seed 3"},
         "fwd_tflops": round(fwd_tflops, 2),
         "fwd_pct_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_pct_peak_in_step": (round(100 * fl["attn_fwd"] / (ms_in_step["attn_fwd"] * 1e-3) / 1e12
+                                       / PEAK_BF16_TFLOPS, 2) if ms_in_step["attn_fwd"] > 0 else None),
         "bwd_tflops": round(bwd_tflops, 2),
         "fwdbwd_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "compute": "fwd bf16 matrix core; bwd fp16 matrix core (dO and dS scaled by powers of two); "
                    "fp32 accumulation and softmax",
-        "kernel_timing": "kernels: HIP events around a replayed HIP graph of `steps` back-to-back "
-                         "launches of each; ms_per_step: the plain loop of `steps` steps; "
-                         "ms_per_step_graph: a replayed graph of `steps` steps",
+        "kernel_timing": "kernels.ms: HIP events around a replayed HIP graph of `steps` back-to-back "
+                         "launches of each; kernels.ms_in_step: a replayed graph of `steps` steps "
+                         "less one of `steps` steps without the kernel; ms_per_step: the plain loop "
+                         "of `steps` steps; ms_per_step_graph: a replayed graph of `steps` steps",
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
